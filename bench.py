@@ -1,0 +1,307 @@
+"""Benchmark of the FP8 block-scaled GEMM path on one MI355X.
+
+Default workload: dense decode, M = 64 tokens, two DeepSeek-V3-shaped layers
+(N=7168, K=2048) and (N=24576, K=1536). One step = the per-token FP8 cast of each
+layer's fp32 activations followed by its block-scaled FP8 GEMM (bf16 out), for both layers.
+Inputs are resident in HBM before timing starts. Each step uses one of R copies of the
+weights (R * |weights| >= 512 MiB) so the 256 MiB Infinity Cache cannot serve them.
+
+Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included),
+`roofline` is for the kernel that takes the most time in the step, measured with HIP
+events on the launch stream over the timed region, and `cpu_baseline` is the CPU oracle
+on the host cores over a bounded sample of the same workload.
+
+Other workloads (--workload prefill|contiguous|masked|tiny) print the same line shape.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP8 block-scaled GEMM TFLOPS & % of MI355X FP8 MFMA peak (dense+grouped, M=64)"
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, published
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
+
+# (kind, shape) per layer of each workload
+WORKLOADS = {
+    "decode": {"desc": "dense decode M=64: (N=7168,K=2048) + (N=24576,K=1536)",
+               "layers": [("dense", dict(M=64, N=7168, K=2048)), ("dense", dict(M=64, N=24576, K=1536))]},
+    "prefill": {"desc": "dense prefill M=4096 with 1% x50 outliers: (N=7168,K=18432) + (N=36864,K=7168)",
+                "layers": [("dense", dict(M=4096, N=7168, K=18432, outliers=True)),
+                           ("dense", dict(M=4096, N=36864, K=7168, outliers=True))]},
+    "contiguous": {"desc": "MoE contiguous G=8, 8192 routed rows padded to 128: (N=4096,K=7168) + (N=7168,K=2048)",
+                   "layers": [("contiguous", dict(G=8, tokens=8192, N=4096, K=7168)),
+                              ("contiguous", dict(G=8, tokens=8192, N=7168, K=2048))]},
+    "masked": {"desc": "MoE masked G=32, M_max=256, valid ~U{0..256}: (N=4096,K=7168) + (N=7168,K=2048)",
+               "layers": [("masked", dict(G=32, M_max=256, N=4096, K=7168)),
+                          ("masked", dict(G=32, M_max=256, N=7168, K=2048))]},
+    "tiny": {"desc": "dense M=128 N=256 K=512", "layers": [("dense", dict(M=128, N=256, K=512))]},
+}
+
+
+def layer_work(kind, s, valid_rows):
+    """Algorithmic flops and HBM bytes of one GEMM launch (valid rows only)."""
+    N, K = s["N"], s["K"]
+    G = s.get("G", 1)
+    flops = 2.0 * valid_rows * N * K
+    byts = (valid_rows * K            # A e4m3
+            + G * N * K               # B e4m3
+            + 4 * valid_rows * K // 128   # activation scales
+            + 4 * G * (N // 128) * (K // 128)  # weight scales
+            + 2 * valid_rows * N)     # bf16 out
+    return flops, float(byts)
+
+
+def cast_bytes(rows, K):
+    return float(rows * K * 4 + rows * K + 4 * rows * K // 128)
+
+
+def build_layer(dg, torch, kind, s, seed, copies):
+    """Device inputs for one layer: fp32 activations, `copies` quantised weight copies."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * seed + 17)
+    N, K = s["N"], s["K"]
+    meta = None
+    if kind == "dense":
+        rows = s["M"]
+        valid = rows
+        a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
+        if s.get("outliers"):
+            hit = torch.rand((rows, K), generator=gen, device=dev) < 0.01
+            a = torch.where(hit, a * 50.0, a)
+        G = 1
+    elif kind == "contiguous":
+        mi, counts = synth.contiguous_layout(s["G"], s["tokens"], seed)
+        rows = mi.size
+        valid = int(counts.sum())
+        a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
+        mi_d = torch.from_numpy(mi).to(dev)
+        a[mi_d < 0] = 0.0
+        meta = mi_d
+        G = s["G"]
+    else:
+        mm = synth.masked_layout(s["G"], s["M_max"], seed)
+        rows = s["G"] * s["M_max"]
+        valid = int(mm.sum())
+        a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
+        meta = torch.from_numpy(mm).to(dev)
+        G = s["G"]
+    ws = []
+    for c in range(copies):
+        w = torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
+        qb, sb = dg.cast_fp8_per_block(w)
+        del w
+        if kind == "dense":
+            ws.append((qb, sb))
+        else:
+            ws.append((qb.view(G, N, K), sb.view(G, N // 128, K // 128)))
+    qa = torch.empty((rows, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((rows, K // 128), dtype=torch.float32, device=dev)
+    if kind == "masked":
+        d = torch.empty((s["G"], s["M_max"], N), dtype=torch.bfloat16, device=dev)
+    else:
+        d = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
+    return dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G)
+
+
+def run_layer(dg, L, copy_idx, ev=None):
+    """Cast activations then GEMM; `ev` (list) receives (label, start, end) event pairs."""
+    import torch
+    kind, s = L["kind"], L["s"]
+    N, K = s["N"], s["K"]
+    qb, sb = L["ws"][copy_idx % len(L["ws"])]
+    e = None
+    if ev is not None:
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+    dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"])
+    if ev is not None:
+        e[1].record()
+    if kind == "dense":
+        dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"])
+    elif kind == "contiguous":
+        dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
+    else:
+        G, Mm = s["G"], s["M_max"]
+        dg.grouped_gemm_masked(L["qa"].view(G, Mm, K), L["sa"].view(G, Mm, K // 128), qb, sb, L["meta"],
+                               expected_m=max(1, L["valid"] // G), d=L["d"])
+    if ev is not None:
+        e[2].record()
+        ev.append(("cast", L, e[0], e[1]))
+        ev.append(("gemm", L, e[1], e[2]))
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "dg_device.h"):
+        with open(os.path.join(ROOT, "moe_grouped_gemm_e4m3_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload, label):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get(workload, {}).get(label)
+    if not rec or rec.get("source_hash") != gemm_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, budget_s):
+    """The CPU oracle (unchanged) on a bounded sample of the workload: every layer's cast
+    and GEMM over a row sample, repeated until ~budget_s seconds of work."""
+    import numpy as np
+    import oracle
+    import synth
+    sample_desc = []
+    jobs = []
+    for li, (kind, s) in enumerate(WORKLOADS[workload]["layers"]):
+        N, K = s["N"], s["K"]
+        rows = {"dense": s.get("M", 64), "contiguous": 64, "masked": 64}[kind]
+        rows = min(rows, 64)
+        a, _ = synth.dense_inputs(rows, 128, K, seed=li)
+        G = s.get("G", 1)
+        bcols = N if kind == "dense" and N * K * rows <= 2 ** 31 else min(N, 2048)
+        b = synth.normal((bcols, K), li, synth.TID_B, 0.02)
+        qb, sb = oracle.cast_per_block(b)
+        jobs.append((a, qb, sb, rows, bcols, K))
+        sample_desc.append("%dx%dx%d" % (rows, bcols, K))
+    flops = 0.0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for a, qb, sb, rows, bcols, K in jobs:
+            qa, sa = oracle.cast_per_token(a)
+            oracle.gemm(qa, sa, qb, sb)
+            flops += 2.0 * rows * bcols * K
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "per-token cast + fp64 GEMM of %s (rows x N x K per layer), %d repetitions in %.1f s"
+                      % (", ".join(sample_desc), reps, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cache-bytes", type=float, default=512 * 2 ** 20,
+                    help="minimum bytes of distinct weight copies cycled through")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see the sharding "
+              "notes in the design document); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_e4m3_amd as dg
+    if not os.path.exists(dg.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    wl = WORKLOADS[args.workload]
+    # weight copies so each step streams its weights from HBM
+    wbytes = sum(s.get("G", 1) * s["N"] * s["K"] for _, s in wl["layers"])
+    copies = int(min(64, max(1, math.ceil(args.cache_bytes / wbytes))))
+    layers = [build_layer(dg, torch, kind, s, args.seed + i, copies) for i, (kind, s) in enumerate(wl["layers"])]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        for L in layers:
+            run_layer(dg, L, i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events around every launch on the current stream
+    ev = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        for L in layers:
+            run_layer(dg, L, args.warmup + i, ev)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per = {}
+    for label, L, e0, e1 in ev:
+        key = (label, id(L))
+        per.setdefault(key, [L, label, 0.0, 0])
+        per[key][2] += e0.elapsed_time(e1)
+        per[key][3] += 1
+    kernels = []
+    step_flops = 0.0
+    for L in layers:
+        f, b = layer_work(L["kind"], L["s"], L["valid"])
+        step_flops += f
+    for (label, _), (L, lab, ms, n) in per.items():
+        avg_us = ms / n * 1e3
+        s = L["s"]
+        if lab == "gemm":
+            f, b = layer_work(L["kind"], s, L["valid"])
+            bound = "hbm" if f / b < RIDGE else "mfma"
+        else:
+            f, b = 0.0, cast_bytes(L["rows"], s["K"])
+            bound = "hbm"
+        kernels.append({"kernel": lab, "layer": "%s N=%d K=%d" % (L["kind"], s["N"], s["K"]), "avg_us": avg_us,
+                        "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9, "bound": bound,
+                        "flops": f, "bytes": b})
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    if dom["bound"] == "hbm":
+        achieved, peak, unit = dom["gbs"], PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dom["tflops"], PEAK_FP8_TFLOPS, "TFLOP/s"
+    traffic = load_traffic(args.workload, dom["layer"] + " " + dom["kernel"])
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": wl["desc"], "weight_copies": copies,
+                   "step": "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM, per layer"},
+        "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5),
+        "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": dom["kernel"] + " " + dom["layer"], "algorithmic_bytes": dom["bytes"],
+                     "algorithmic_flops": dom["flops"], "avg_us": round(dom["avg_us"], 3)},
+        "kernels": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in kk.items()} for kk in kernels],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+        out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

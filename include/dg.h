@@ -1,0 +1,157 @@
+/*
+ * dg.h - C ABI of the FP8 (e4m3) block-scaled GEMM library for MI355X (gfx950).
+ *
+ * The method (DeepGEMM-style fine-grained FP8 scaling):
+ *   - activations: FP8 e4m3 with one fp32 scale per token per 128 consecutive K
+ *     elements ("1x128"); weights: FP8 e4m3 with one fp32 scale per 128x128 block.
+ *     DeepGEMM article, section "FP8 and fine-grained scaling" (activations scaled per
+ *     slice, weights per matrix block, accumulation kept in higher precision);
+ *     DeepSeek-V3 repo review, "Innovations" item 4 (one scale per 128 elements) and
+ *     "Solution philosophy" (128x128 block scaling).
+ *   - the GEMM multiplies within each 128-wide K block on FP8 matrix hardware, then
+ *     promotes the partial sum to fp32, multiplies it by scale_a * scale_b and
+ *     accumulates: DeepGEMM launch write-up, "Built for modern AI compute" (two-level
+ *     accumulation) and "Deployment guide" (promotion outside the matrix units).
+ *   - normal (dense) GEMM plus MoE grouped GEMM in a contiguous layout (groups stacked
+ *     along M) and a masked layout (per-group valid-row count, the format a
+ *     communication library hands over): DeepGEMM article, section "~300-line JIT
+ *     core"; DeepGEMM launch write-up, "Performance" (the three table headings).
+ *   - quantisation bound 448 (OCP E4M3FN max finite): DeepSeek-V3 repo review,
+ *     "Risks and shortcomings" item 6.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller, contiguous, row-major,
+ *     and 16-byte aligned. The library never allocates, frees or keeps a pointer.
+ *   - FP8 tensors are raw OCP E4M3FN bytes (uint8_t); bf16 tensors are raw uint16_t bits.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls only
+ *     enqueue work on it and return without synchronising; inputs must stay alive
+ *     until the stream has run the work.
+ *   - "NT": A is [M,K] and B is [N,K], both K-major, and D = A * B^T.
+ *   - K and N must be multiples of 128. M may be any value >= 0.
+ *   - Arguments the host can see are validated before anything is enqueued. On an error
+ *     nothing is launched, outputs are untouched, and the status says why;
+ *     dg_last_error_message() gives a thread-local detail string.
+ *   - Empty problems (M = 0, G = 0) enqueue nothing and return DG_OK.
+ *   - Device-resident metadata (m_indices, masked_m) is not validated on the host; see
+ *     each entry point.
+ *   - Calls are thread-safe; the only shared state is a once-initialised record of the
+ *     current device's architecture.
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, unknown dtype */
+  DG_ERR_UNSUPPORTED_SHAPE = 2, /* K or N not a multiple of 128, M_total not a multiple of 128 */
+  DG_ERR_MISALIGNED = 3,        /* a pointer not 16-byte aligned */
+  DG_ERR_UNSUPPORTED_DEVICE = 4, /* current device is not gfx950, or no device */
+  DG_ERR_LAUNCH = 5             /* the kernel launch failed */
+} dg_status_t;
+
+typedef enum { DG_INPUT_F32 = 0, DG_INPUT_BF16 = 1 } dg_input_dtype_t;
+
+/*
+ * Per-token FP8 cast of activations (DeepSeek-V3 repo review, "Innovations" item 4:
+ * one scale per 128 elements; "Risks" item 6: bound 448).
+ *   x  [M,K]  fp32 or bf16 (x_dtype), finite values.
+ *   q  [M,K]  e4m3 bytes (output).
+ *   sf [M,K/128] fp32 scales (output).
+ * For each row m and chunk j = columns [128j, 128j+128):
+ *   amax = max |x|; s = amax / 448 (correctly rounded fp32 division);
+ *   q = e4m3(x / s) with correctly rounded division, round-to-nearest-even, saturation
+ *   to +-448, the sign of zero kept; if s == 0 the chunk gets s = 0 and signed zeros.
+ * Requires K % 128 == 0.
+ */
+dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t M, int64_t K,
+                                  uint8_t* q, float* sf, void* stream);
+
+/*
+ * Per-block FP8 cast of weights: the same rule as above with the amax taken over each
+ * 128x128 block (DeepSeek-V3 repo review, "Solution philosophy": 128x128 block scaling).
+ *   w  [N,K] fp32 or bf16; q [N,K] e4m3 (output); sf [N/128, K/128] fp32 (output).
+ * Requires N % 128 == 0 and K % 128 == 0. For a grouped weight tensor [G,N,K] pass
+ * N' = G*N (blocks never straddle groups because N % 128 == 0).
+ */
+dg_status_t dg_cast_fp8_per_block(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K,
+                                  uint8_t* q, float* sf, void* stream);
+
+/*
+ * Dense FP8 GEMM with fine-grained scaling (DeepGEMM article, "~300-line JIT core";
+ * launch write-up, "Performance": normal GEMM for dense models).
+ *   a   [M,K] e4m3,      sfa [M, K/128] fp32 (per-token scales)
+ *   b   [N,K] e4m3,      sfb [N/128, K/128] fp32 (block scales)
+ *   d   [M,N] bf16 (output):
+ *   d[m,n] = bf16_rne( sum_kb  P_kb[m,n] * sfa[m,kb] * sfb[n/128,kb] ),
+ *   P_kb = the FP8 product sum over K block kb, promoted to fp32 once per block.
+ * Requires N % 128 == 0, K % 128 == 0.
+ */
+dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * MoE grouped GEMM, contiguous layout (DeepGEMM article, "~300-line JIT core": groups
+ * formed dynamically along M; launch write-up, "Performance": contiguous layout).
+ *   a [M_total,K] e4m3, sfa [M_total,K/128]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
+ *   m_indices [M_total] int32 (device): expert id of each row, or -1 for padding;
+ *   d [M_total,N] bf16 (output).
+ * Each aligned 128-row block belongs to one expert: the expert of the block's first row.
+ * A block whose first row is -1 is skipped (its rows of d are left untouched). Rows
+ * marked -1 inside a computed block get unspecified values. Values outside [-1, G) and
+ * blocks mixing experts are undefined behaviour (not checked on the device).
+ * Requires M_total % 128 == 0, N % 128 == 0, K % 128 == 0, G >= 1.
+ */
+dg_status_t dg_grouped_gemm_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                       const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                       int32_t G, int64_t M_total, int64_t N, int64_t K,
+                                       void* stream);
+
+/*
+ * MoE grouped GEMM, masked layout (DeepGEMM article, "~300-line JIT core": the masked
+ * layout interfaces with the communication library; launch write-up, "Performance").
+ *   a [G,M_max,K] e4m3, sfa [G,M_max,K/128]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
+ *   masked_m [G] int32 (device): valid rows of each group, clamped to [0, M_max];
+ *   d [G,M_max,N] bf16 (output).
+ * Rows r < masked_m[g] of group g are computed; rows r >= masked_m[g] are not written.
+ * expected_m is a host-side hint of the typical masked_m (0 = unknown) that only selects
+ * the kernel schedule; results do not depend on it.
+ * Requires N % 128 == 0, K % 128 == 0, G >= 0, M_max >= 0.
+ */
+dg_status_t dg_grouped_gemm_masked(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                   const float* sfb, const int32_t* masked_m, uint16_t* d,
+                                   int32_t G, int64_t M_max, int64_t N, int64_t K,
+                                   int64_t expected_m, void* stream);
+
+/*
+ * The three GEMMs above with the kernel schedule chosen by the caller (for tuning and
+ * for tests that must cover every schedule on the same problem). Same math, same
+ * arguments and same validation as the named entry points.
+ *   layout:   0 = dense (meta ignored, G ignored), 1 = contiguous (meta = m_indices),
+ *             2 = masked (meta = masked_m).
+ *   schedule: 0 = automatic (what the named entry points use), 1 = decode (64-row
+ *             blocks, K split over the waves of a workgroup; dense and masked only),
+ *             2 = 128x128 LDS-staged tiles, 3 = 256x128 LDS-staged tiles (dense and
+ *             masked only). A schedule a layout does not support falls back to 2.
+ */
+dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, const uint8_t* a, const float* sfa,
+                                  const uint8_t* b, const float* sfb, const int32_t* meta, uint16_t* d,
+                                  int32_t G, int64_t M, int64_t N, int64_t K, int64_t expected_m,
+                                  void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* dg_status_string(dg_status_t status);
+
+/* Detail of the last failed call on this thread (static per-thread buffer; "" if none). */
+const char* dg_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

@@ -1,0 +1,191 @@
+"""Thin Python binding over libdg.so, the C ABI declared in include/dg.h.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libdg.so.
+PyTorch supplies device memory and the current stream; FP8 tensors travel as torch.uint8
+(raw OCP E4M3FN bytes) and bf16 outputs as torch.bfloat16. There is no CPU fallback:
+if libdg.so is missing or fails to load, every call raises.
+
+Entry points (same names as the C ABI, without the dg_ prefix):
+  cast_fp8_per_token(x)                      -> (q [M,K] uint8, sf [M,K/128] fp32)
+  cast_fp8_per_block(w)                      -> (q [N,K] uint8, sf [N/128,K/128] fp32)
+  gemm_fp8_nt(a, sfa, b, sfb)                -> d [M,N] bf16
+  grouped_gemm_contiguous(a, sfa, b, sfb, m_indices)      -> d [M_total,N] bf16
+  grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m) -> d [G,M_max,N] bf16
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdg.so")
+
+DG_OK = 0
+STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARGUMENT", 2: "DG_ERR_UNSUPPORTED_SHAPE",
+                3: "DG_ERR_MISALIGNED", 4: "DG_ERR_UNSUPPORTED_DEVICE", 5: "DG_ERR_LAUNCH"}
+LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+SCHED_AUTO, SCHED_DECODE, SCHED_TILE128, SCHED_TILE256 = 0, 1, 2, 3
+INPUT_F32, INPUT_BF16 = 0, 1
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdg.so (built by moe_grouped_gemm_e4m3_amd.build); raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libdg.so is not built: run `python -m moe_grouped_gemm_e4m3_amd.build` "
+                              "or __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.dg_cast_fp8_per_token.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
+        L.dg_cast_fp8_per_block.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
+        L.dg_gemm_fp8_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+        L.dg_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+        L.dg_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        L.dg_gemm_fp8_scheduled.argtypes = [I32, I32, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        for fn in ("dg_cast_fp8_per_token", "dg_cast_fp8_per_block", "dg_gemm_fp8_nt",
+                   "dg_grouped_gemm_contiguous", "dg_grouped_gemm_masked", "dg_gemm_fp8_scheduled"):
+            getattr(L, fn).restype = ctypes.c_int
+        L.dg_status_string.argtypes = [ctypes.c_int]
+        L.dg_status_string.restype = ctypes.c_char_p
+        L.dg_last_error_message.argtypes = []
+        L.dg_last_error_message.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != DG_OK:
+        raise DGError(status, lib().dg_last_error_message().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+# ---- casts ---------------------------------------------------------------------------
+def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None):
+    """x [M,K] fp32/bf16 -> (q [M,K] uint8 e4m3, sf [M,K/128] fp32)."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, x.dtype, "x")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
+    sf = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if sf is None else sf
+    dt = INPUT_BF16 if x.dtype == torch.bfloat16 else INPUT_F32
+    _check(lib().dg_cast_fp8_per_token(_ptr(x), dt, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
+    return q, sf
+
+
+def cast_fp8_per_block(w: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None):
+    """w [N,K] or [G,N,K] fp32/bf16 -> (q uint8 e4m3 same shape, sf [..., N/128, K/128] fp32)."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("w must be float32 or bfloat16")
+    _need(w, w.dtype, "w")
+    lead = tuple(w.shape[:-2])
+    N, K = w.shape[-2:]
+    rows = N
+    for s in lead:
+        rows *= s
+    q = torch.empty(w.shape, dtype=torch.uint8, device=w.device) if q is None else q
+    sf = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=w.device) if sf is None else sf
+    dt = INPUT_BF16 if w.dtype == torch.bfloat16 else INPUT_F32
+    _check(lib().dg_cast_fp8_per_block(_ptr(w), dt, rows, K, _ptr(q), _ptr(sf), _stream(w.device)))
+    return q, sf
+
+
+# ---- GEMMs ---------------------------------------------------------------------------
+def _operands(a, sfa, b, sfb):
+    _need(a, torch.uint8, "a")
+    _need(sfa, torch.float32, "sfa")
+    _need(b, torch.uint8, "b")
+    _need(sfb, torch.float32, "sfb")
+
+
+def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = SCHED_AUTO):
+    """a [M,K] e4m3, sfa [M,K/128], b [N,K] e4m3, sfb [N/128,K/128] -> d [M,N] bf16 = A * B^T."""
+    _operands(a, sfa, b, sfb)
+    M, K = a.shape
+    N = b.shape[0]
+    if tuple(b.shape) != (N, K) or tuple(sfa.shape) != (M, K // 128) or tuple(sfb.shape) != (N // 128, K // 128):
+        raise ValueError("shape mismatch: a %s sfa %s b %s sfb %s" % (tuple(a.shape), tuple(sfa.shape),
+                                                                    tuple(b.shape), tuple(sfb.shape)))
+    d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
+    _need(d, torch.bfloat16, "d")
+    if schedule == SCHED_AUTO:
+        st = lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), M, N, K, _stream(a.device))
+    else:
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_DENSE, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), None,
+                                         _ptr(d), 1, M, N, K, 0, _stream(a.device))
+    _check(st)
+    return d
+
+
+def grouped_gemm_contiguous(a, sfa, b, sfb, m_indices, d: torch.Tensor | None = None,
+                            schedule: int = SCHED_AUTO):
+    """a [M_total,K], sfa [M_total,K/128], b [G,N,K], sfb [G,N/128,K/128], m_indices [M_total]
+    int32 (expert id or -1) -> d [M_total,N] bf16."""
+    _operands(a, sfa, b, sfb)
+    _need(m_indices, torch.int32, "m_indices")
+    M, K = a.shape
+    G, N, _ = b.shape
+    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (M, K // 128)
+            or tuple(sfb.shape) != (G, N // 128, K // 128) or tuple(m_indices.shape) != (M,)):
+        raise ValueError("shape mismatch")
+    d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
+    _need(d, torch.bfloat16, "d")
+    if schedule == SCHED_AUTO:
+        st = lib().dg_grouped_gemm_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d),
+                                              G, M, N, K, _stream(a.device))
+    else:
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_CONTIGUOUS, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb),
+                                         _ptr(m_indices), _ptr(d), G, M, N, K, 0, _stream(a.device))
+    _check(st)
+    return d
+
+
+def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.Tensor | None = None,
+                        schedule: int = SCHED_AUTO):
+    """a [G,M_max,K], sfa [G,M_max,K/128], b [G,N,K], sfb [G,N/128,K/128], masked_m [G] int32
+    -> d [G,M_max,N] bf16 (rows >= masked_m[g] are left untouched)."""
+    _operands(a, sfa, b, sfb)
+    _need(masked_m, torch.int32, "masked_m")
+    G, M, K = a.shape
+    N = b.shape[1]
+    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (G, M, K // 128)
+            or tuple(sfb.shape) != (G, N // 128, K // 128) or tuple(masked_m.shape) != (G,)):
+        raise ValueError("shape mismatch")
+    d = torch.empty((G, M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
+    _need(d, torch.bfloat16, "d")
+    if schedule == SCHED_AUTO:
+        st = lib().dg_grouped_gemm_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
+                                          G, M, N, K, expected_m, _stream(a.device))
+    else:
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_MASKED, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb),
+                                         _ptr(masked_m), _ptr(d), G, M, N, K, expected_m, _stream(a.device))
+    _check(st)
+    return d

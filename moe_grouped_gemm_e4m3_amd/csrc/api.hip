@@ -1,0 +1,173 @@
+// api.hip - the C ABI declared in include/dg.h: argument validation (before any HIP
+// call), device check, schedule dispatch, status reporting.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "dg.h"
+#include "dg_launch.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+dg_status_t fail(dg_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dg_status_t ok() {
+  g_msg[0] = '\0';
+  return DG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kQ = 128;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // sizes stay below 2^31 per dimension
+
+// Once per device: is it gfx950? Cached under a mutex (the only shared state).
+dg_status_t check_device() {
+  static std::mutex mu;
+  static signed char cache[64];  // 0 unknown, 1 yes, -1 no
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(DG_ERR_UNSUPPORTED_DEVICE, "no HIP device is current");
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 64 && cache[dev] != 0)
+    return cache[dev] > 0 ? DG_OK : fail(DG_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(DG_ERR_UNSUPPORTED_DEVICE, "cannot query device %d", dev);
+  const bool yes = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev] = yes ? 1 : -1;
+  return yes ? DG_OK : fail(DG_ERR_UNSUPPORTED_DEVICE, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+}
+
+dg_status_t launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DG_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+dg_status_t check_nk(int64_t N, int64_t K) {
+  if (N < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "negative size (N=%lld, K=%lld)", (long long)N, (long long)K);
+  if (N % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "N=%lld is not a multiple of 128", (long long)N);
+  if (K % kQ != 0 || K == 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "K=%lld is not a positive multiple of 128", (long long)K);
+  if (N >= kMaxDim || K >= kMaxDim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "N or K >= 2^31");
+  return DG_OK;
+}
+
+// Common part of the three GEMM entry points.
+dg_status_t run_gemm(dg::Layout layout, int schedule, const uint8_t* a, const float* sfa, const uint8_t* b,
+                     const float* sfb, const int32_t* meta, uint16_t* d, int64_t G, int64_t M, int64_t N,
+                     int64_t K, int64_t expected_m, void* stream, const char* name) {
+  if (M < 0 || G < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
+  dg_status_t st = check_nk(N, K);
+  if (st != DG_OK) return st;
+  if (M >= kMaxDim || G >= kMaxDim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: M or G >= 2^31", name);
+  if (layout == dg::Layout::Contiguous) {
+    if (M % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: M_total=%lld is not a multiple of 128", name, (long long)M);
+    if (G < 1) return fail(DG_ERR_INVALID_ARGUMENT, "%s: G must be >= 1", name);
+  }
+  if (schedule < 0 || schedule > 3) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown schedule %d", name, schedule);
+  if (M == 0 || N == 0 || G == 0) return ok();
+  if (!a || !sfa || !b || !sfb || !d || (layout != dg::Layout::Dense && !meta))
+    return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(d) ||
+      (meta && !aligned16(meta)))
+    return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  st = check_device();
+  if (st != DG_OK) return st;
+  dg::GemmProblem p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  p.m_indices = layout == dg::Layout::Contiguous ? meta : nullptr;
+  p.masked_m = layout == dg::Layout::Masked ? meta : nullptr;
+  p.M = M; p.N = N; p.K = K; p.G = (int32_t)G; p.layout = layout;
+  const char* chosen = "";
+  hipError_t e = dg::launch_gemm(p, static_cast<dg::Schedule>(schedule), expected_m,
+                                 static_cast<hipStream_t>(stream), &chosen);
+  if (getenv("DG_LOG")) fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
+                                (long long)N, (long long)K, (long long)G, chosen);
+  return launched(e, name);
+}
+
+dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int64_t rows, int64_t K,
+                     uint8_t* q, float* sf, void* stream) {
+  const char* name = per_block ? "dg_cast_fp8_per_block" : "dg_cast_fp8_per_token";
+  if (dtype != DG_INPUT_F32 && dtype != DG_INPUT_BF16) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, (int)dtype);
+  if (rows < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
+  if (K % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld is not a multiple of 128", name, (long long)K);
+  if (per_block && rows % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: N=%lld is not a multiple of 128", name, (long long)rows);
+  if (rows >= kMaxDim || K >= kMaxDim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: size >= 2^31", name);
+  if (rows == 0 || K == 0) return ok();
+  if (!x || !q || !sf) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  dg_status_t st = check_device();
+  if (st != DG_OK) return st;
+  hipError_t e = per_block ? dg::launch_cast_per_block(x, dtype == DG_INPUT_BF16, rows, K, q, sf, static_cast<hipStream_t>(stream))
+                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, rows, K, q, sf, static_cast<hipStream_t>(stream));
+  return launched(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t M, int64_t K, uint8_t* q,
+                                  float* sf, void* stream) {
+  return run_cast(false, x, x_dtype, M, K, q, sf, stream);
+}
+
+dg_status_t dg_cast_fp8_per_block(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K, uint8_t* q,
+                                  float* sf, void* stream) {
+  return run_cast(true, w, w_dtype, N, K, q, sf, stream);
+}
+
+dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                           int64_t M, int64_t N, int64_t K, void* stream) {
+  return run_gemm(dg::Layout::Dense, 0, a, sfa, b, sfb, nullptr, d, 1, M, N, K, 0, stream, "dg_gemm_fp8_nt");
+}
+
+dg_status_t dg_grouped_gemm_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                       const int32_t* m_indices, uint16_t* d, int32_t G, int64_t M_total,
+                                       int64_t N, int64_t K, void* stream) {
+  return run_gemm(dg::Layout::Contiguous, 0, a, sfa, b, sfb, m_indices, d, G, M_total, N, K, 0, stream,
+                  "dg_grouped_gemm_contiguous");
+}
+
+dg_status_t dg_grouped_gemm_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                   const int32_t* masked_m, uint16_t* d, int32_t G, int64_t M_max, int64_t N,
+                                   int64_t K, int64_t expected_m, void* stream) {
+  return run_gemm(dg::Layout::Masked, 0, a, sfa, b, sfb, masked_m, d, G, M_max, N, K, expected_m, stream,
+                  "dg_grouped_gemm_masked");
+}
+
+dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, const uint8_t* a, const float* sfa,
+                                  const uint8_t* b, const float* sfb, const int32_t* meta, uint16_t* d, int32_t G,
+                                  int64_t M, int64_t N, int64_t K, int64_t expected_m, void* stream) {
+  if (layout < 0 || layout > 2) return fail(DG_ERR_INVALID_ARGUMENT, "dg_gemm_fp8_scheduled: unknown layout %d", layout);
+  const dg::Layout L = static_cast<dg::Layout>(layout);
+  return run_gemm(L, schedule, a, sfa, b, sfb, L == dg::Layout::Dense ? nullptr : meta, d,
+                  L == dg::Layout::Dense ? 1 : G, M, N, K, expected_m, stream, "dg_gemm_fp8_scheduled");
+}
+
+const char* dg_status_string(dg_status_t status) {
+  switch (status) {
+    case DG_OK: return "DG_OK";
+    case DG_ERR_INVALID_ARGUMENT: return "DG_ERR_INVALID_ARGUMENT";
+    case DG_ERR_UNSUPPORTED_SHAPE: return "DG_ERR_UNSUPPORTED_SHAPE";
+    case DG_ERR_MISALIGNED: return "DG_ERR_MISALIGNED";
+    case DG_ERR_UNSUPPORTED_DEVICE: return "DG_ERR_UNSUPPORTED_DEVICE";
+    case DG_ERR_LAUNCH: return "DG_ERR_LAUNCH";
+  }
+  return "DG_ERR_UNKNOWN";
+}
+
+const char* dg_last_error_message(void) { return g_msg; }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// dg_launch.h - internal interface between the C-ABI layer (api.hip) and the kernel
+// translation units. Host-side only; no HIP types beyond hipStream_t / hipError_t.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+// Which operand layout a GEMM launch serves.
+enum class Layout : int { Dense = 0, Contiguous = 1, Masked = 2 };
+
+// One GEMM problem as the kernels see it. For Dense, G = 1. For Contiguous, rows of a/d
+// are M_total = M and b/sfb are [G,N,K] / [G,N/128,K/128]. For Masked, a/sfa/d hold G
+// groups of M rows each (M = M_max).
+struct GemmProblem {
+  const uint8_t* a;
+  const float* sfa;
+  const uint8_t* b;
+  const float* sfb;
+  uint16_t* d;
+  const int32_t* m_indices;  // Contiguous only
+  const int32_t* masked_m;   // Masked only
+  int64_t M, N, K;
+  int32_t G;
+  Layout layout;
+};
+
+// Kernel schedules. Decode: 64-row M blocks, K split across the waves of a workgroup,
+// operands streamed straight into registers. Tile: LDS-staged, double-buffered tiles.
+enum class Schedule : int { Auto = 0, Decode = 1, Tile128 = 2, Tile256 = 3 };
+
+hipError_t launch_gemm(const GemmProblem& p, Schedule s, int64_t expected_m, hipStream_t stream,
+                       const char** chosen);
+
+hipError_t launch_cast_per_token(const void* x, int bf16, int64_t M, int64_t K, uint8_t* q, float* sf,
+                                 hipStream_t stream);
+hipError_t launch_cast_per_block(const void* w, int bf16, int64_t N, int64_t K, uint8_t* q, float* sf,
+                                 hipStream_t stream);
+
+}  // namespace dg

@@ -1,0 +1,102 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point include/dg.h
+declares, and rejects bad arguments before any HIP call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import moe_grouped_gemm_e4m3_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from moe_grouped_gemm_e4m3_amd import build
+        build.build()
+    return m.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("dg_cast_fp8_per_token", "dg_gemm_fp8_nt", "dg_grouped_gemm_contiguous",
+              "dg_grouped_gemm_masked", "dg_status_string", "dg_last_error_message"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in [(0, b"DG_OK"), (1, b"DG_ERR_INVALID_ARGUMENT"), (2, b"DG_ERR_UNSUPPORTED_SHAPE"),
+                       (3, b"DG_ERR_MISALIGNED"), (4, b"DG_ERR_UNSUPPORTED_DEVICE"), (5, b"DG_ERR_LAUNCH")]:
+        assert L.dg_status_string(code) == name
+
+
+P = 0x10000  # an aligned fake address: validation never dereferences pointers
+Q = 0x10001  # misaligned
+
+
+def _gemm(L, a=P, sfa=P, b=P, sfb=P, d=P, M=64, N=256, K=512):
+    return L.dg_gemm_fp8_nt(a, sfa, b, sfb, d, M, N, K, None)
+
+
+def test_gemm_argument_errors(L):
+    assert _gemm(L, K=500) == 2
+    assert _gemm(L, K=0) == 2
+    assert _gemm(L, N=200) == 2
+    assert _gemm(L, M=-1) == 1
+    assert _gemm(L, N=-128) == 1
+    assert _gemm(L, a=None) == 1
+    assert _gemm(L, d=None) == 1
+    assert _gemm(L, sfb=Q) == 3
+    assert b"16-byte" in L.dg_last_error_message()
+    assert _gemm(L, M=0) == 0          # empty: nothing to do, nothing touched
+    assert _gemm(L, M=0, a=None) == 0
+    assert L.dg_last_error_message() == b""
+
+
+def test_gemm_without_gpu_reports_device(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _gemm(L) == 4  # arguments valid, no gfx950 device: nothing launched
+
+
+def test_grouped_argument_errors(L):
+    c = L.dg_grouped_gemm_contiguous
+    assert c(P, P, P, P, P, P, 4, 1000, 256, 512, None) == 2   # M_total % 128
+    assert c(P, P, P, P, P, P, 0, 1024, 256, 512, None) == 1   # G < 1
+    assert c(P, P, P, P, None, P, 4, 1024, 256, 512, None) == 1  # m_indices null
+    assert c(P, P, P, P, P, P, 4, 0, 256, 512, None) == 0
+    m = L.dg_grouped_gemm_masked
+    assert m(P, P, P, P, P, P, 4, 64, 256, 500, 0, None) == 2
+    assert m(P, P, P, P, P, P, -1, 64, 256, 512, 0, None) == 1
+    assert m(P, P, P, P, P, P, 0, 64, 256, 512, 0, None) == 0  # G = 0: empty
+    assert m(P, P, P, P, None, P, 4, 64, 256, 512, 0, None) == 1
+    assert m(P, P, P, P, Q, P, 4, 64, 256, 512, 0, None) == 3
+    s = L.dg_gemm_fp8_scheduled
+    assert s(7, 0, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
+    assert s(0, 9, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
+
+
+def test_cast_argument_errors(L):
+    t = L.dg_cast_fp8_per_token
+    assert t(P, 0, 64, 500, P, P, None) == 2
+    assert t(P, 2, 64, 512, P, P, None) == 1  # unknown dtype
+    assert t(None, 0, 64, 512, P, P, None) == 1
+    assert t(P, 0, 64, 512, Q, P, None) == 3
+    assert t(P, 0, 0, 512, P, P, None) == 0
+    b = L.dg_cast_fp8_per_block
+    assert b(P, 0, 100, 512, P, P, None) == 2
+    assert b(P, 1, 128, 384, P, Q, None) == 3
