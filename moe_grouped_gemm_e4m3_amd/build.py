@@ -24,6 +24,8 @@ FLAGS = [
     # fp32 subnormals kept and divisions correctly rounded: the cast is bit-exact
     "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wno-unused-command-line-argument",
+    # MFMA results straight into VGPRs: the promotion FMA reads them without AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

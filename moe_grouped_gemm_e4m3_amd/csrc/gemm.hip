@@ -18,6 +18,9 @@
 //    double-buffered LDS (16-byte chunks XOR-swizzled by row to spread banks), 64x64
 //    wave tiles of 4x4 MFMAs, a grouped raster of tiles and an XCD-aware workgroup remap
 //    so neighbouring tiles share an L2.
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "dg_device.h"
 #include "dg_launch.h"
 
@@ -42,23 +45,37 @@ struct KParams {
 
 __device__ __forceinline__ int64_t clamp_rows(int64_t v, int64_t hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
 
-// 32 bytes of one operand row for MFMA lane group (l >> 4): two 16-byte global loads.
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// K split of one 128-byte operand row over the four lane groups g = l >> 4 of an MFMA:
+// group g holds bytes [16g, 16g+16) and [64+16g, 64+16g+16). A and B use the same split,
+// so the products pair up; each 16-byte load instruction of a wave then covers whole
+// 64-byte halves of 16 rows.
 __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
   const v4i lo = *reinterpret_cast<const v4i*>(p);
-  const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 64);
   return cat8(lo, hi);
 }
 
 // ---------------------------------------------------------------------------------
 // decode schedule
 // ---------------------------------------------------------------------------------
-template <int BN, int NW, Layout L>
+// Workgroup: 64 rows x BN columns, NW waves. Wave w owns K blocks kb = w + NW*(KPW*r + i),
+// i < KPW, in rounds r. Within a round every load (A and B fragments, both scales) is
+// issued before the first MFMA, so a wave keeps KPW K blocks of operands in flight; a
+// K block past the end reloads the last block and is weighted by zero.
+template <int BN, int NW, int KPW, Layout L>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
   static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
   static_assert(BN % 16 == 0 && kQ % BN == 0, "tile must sit inside one weight-scale block");
   constexpr int TN = BN / 16;
   __shared__ __attribute__((aligned(16))) float red[NW][64 * BN];
-  __shared__ __attribute__((aligned(16))) float sa_x[NW][64];
+  __shared__ __attribute__((aligned(16))) float sa_x[NW][KPW][64];
 
   const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
   const int mb = (int)(wg % (uint32_t)p.tiles_m);
@@ -79,7 +96,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
   uint16_t* D = p.d + (int64_t)g * p.M * p.N;
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int kof = (l >> 4) * 32;
+  const int kof = (l >> 4) * 16;
   const uint8_t* arow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) arow[i] = A + clamp_rows(m0 + 16 * i + (l & 15), valid - 1) * K + kof;
@@ -87,7 +104,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) brow[j] = B + (n0 + 16 * j + (l & 15)) * K + kof;
   const float* sarow = SA + clamp_rows(m0 + l, valid - 1) * nkb;
-  float* my_sa = sa_x[w];
 
   v4f acc[4][TN];
 #pragma unroll
@@ -95,52 +111,40 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v8i af[4], bf[TN];
-  float sam = 0.f, sbv = 0.f;
-  int kb = w;
-  if (kb < nkb) {
+  for (int base = w; base < nkb; base += NW * KPW) {
+    v8i af[KPW][4], bf[KPW][TN];
+    float sam[KPW], sbv[KPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = load_frag_global(arow[i] + (int64_t)kb * kQ);
+    for (int u = 0; u < KPW; ++u) {
+      const int kb = base + NW * u;
+      const int kc = kb < nkb ? kb : nkb - 1;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = load_frag_global(brow[j] + (int64_t)kb * kQ);
-    sam = sarow[kb];
-    sbv = SB[kb];
-  }
-  while (kb < nkb) {
-    const int kn = kb + NW;
-    v8i af2[4], bf2[TN];
-    float sam2 = 0.f, sbv2 = 0.f;
-    if (kn < nkb) {
+      for (int j = 0; j < TN; ++j) bf[u][j] = load_frag_global(brow[j] + (int64_t)kc * kQ);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af2[i] = load_frag_global(arow[i] + (int64_t)kn * kQ);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bf2[j] = load_frag_global(brow[j] + (int64_t)kn * kQ);
-      sam2 = sarow[kn];
-      sbv2 = SB[kn];
+      for (int i = 0; i < 4; ++i) af[u][i] = load_frag_global(arow[i] + (int64_t)kc * kQ);
+      sam[u] = sarow[kc];
+      sbv[u] = kb < nkb ? SB[kc] : 0.0f;
     }
-    // this lane's 4 output rows of strip i are 16*i + 4*(l>>4) + r: fetch their
-    // activation scales through the wave's private LDS slot
-    my_sa[l] = sam;
+    // this lane's output rows of strip i are 16*i + 4*(l>>4) + r: route the activation
+    // scales there through the wave's private LDS slots
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 s4 = *reinterpret_cast<const float4*>(&my_sa[16 * i + 4 * (l >> 4)]);
-      const float t0 = s4.x * sbv, t1 = s4.y * sbv, t2 = s4.z * sbv, t3 = s4.w * sbv;
+    for (int u = 0; u < KPW; ++u) sa_x[w][u][l] = sam[u];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4f pp = mfma_f8_16x16x128(af[i], bf[j]);
-        acc[i][j][0] = fmaf(pp[0], t0, acc[i][j][0]);
-        acc[i][j][1] = fmaf(pp[1], t1, acc[i][j][1]);
-        acc[i][j][2] = fmaf(pp[2], t2, acc[i][j][2]);
-        acc[i][j][3] = fmaf(pp[3], t3, acc[i][j][3]);
+    for (int u = 0; u < KPW; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 s4 = *reinterpret_cast<const float4*>(&sa_x[w][u][16 * i + 4 * (l >> 4)]);
+        const float t0 = s4.x * sbv[u], t1 = s4.y * sbv[u], t2 = s4.z * sbv[u], t3 = s4.w * sbv[u];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v4f pp = mfma_f8_16x16x128(af[u][i], bf[u][j]);
+          acc[i][j][0] = fmaf(pp[0], t0, acc[i][j][0]);
+          acc[i][j][1] = fmaf(pp[1], t1, acc[i][j][1]);
+          acc[i][j][2] = fmaf(pp[2], t2, acc[i][j][2]);
+          acc[i][j][3] = fmaf(pp[3], t3, acc[i][j][3]);
+        }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = af2[i];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bf[j] = bf2[j];
-    sam = sam2;
-    sbv = sbv2;
-    kb = kn;
   }
 
   // cross-wave reduction of the split-K partial tiles
@@ -168,6 +172,190 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
       o.y = bf16_rne(s.z) | (bf16_rne(s.w) << 16);
       *reinterpret_cast<uint2*>(D + (m0 + row) * p.N + n0 + c4) = o;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// decode schedule with the activation block resident in LDS
+// ---------------------------------------------------------------------------------
+// For M <= 64 and 64*K bytes that fit in LDS: a workgroup first copies its 64 x K
+// activation block (and its scales) into LDS once, with direct global->LDS loads, then
+// streams the weight columns of its share of the output. The column range is cut into
+// units of 16*TN columns; KSPLIT waves share a unit, each summing every KSPLIT-th K
+// block, and NW/KSPLIT units are in flight at once. Every weight byte is read once; the
+// activation block is read once per workgroup instead of once per column tile.
+// LDS: A as [K block][64 rows][128 bytes] with 16-byte chunks XOR-swizzled by row,
+// then the activation scales [K block][64 rows], then (KSPLIT-1) partial tiles per slot.
+template <int TN, int KSPLIT, int NW, int KW, Layout L>
+__global__ __launch_bounds__(64 * NW) void gemm_decode_lds_kernel(KParams p) {
+  static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
+  static_assert(NW % KSPLIT == 0, "waves split evenly over unit slots");
+  constexpr int SLOTS = NW / KSPLIT;
+  constexpr int UW = 16 * TN;  // columns per unit
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
+  const int part = (int)(wg % (uint32_t)p.tiles_n);
+  const int mb = (int)((wg / (uint32_t)p.tiles_n) % (uint32_t)p.tiles_m);
+  const int g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  const int64_t m0 = (int64_t)mb * 64;
+  int64_t valid = p.M;
+  if constexpr (L == Layout::Masked) valid = clamp_rows(p.masked_m[g], p.M);
+  if (m0 >= valid) return;  // uniform over the workgroup
+  const int nkb = p.nkb;
+  const int64_t K = p.K;
+  const int units = (int)(p.N / UW);
+  const int u0 = (int)((int64_t)units * part / p.tiles_n);
+  const int u1 = (int)((int64_t)units * (part + 1) / p.tiles_n);
+
+  const uint8_t* A = p.a + (int64_t)g * p.M * K;
+  const float* SA = p.sfa + (int64_t)g * p.M * nkb;
+  const uint8_t* B = p.b + (int64_t)g * p.N * K;
+  const float* SBg = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
+  uint16_t* D = p.d + (int64_t)g * p.M * p.N;
+
+  uint8_t* sA = smem;
+  float* sSa = reinterpret_cast<float*>(smem + 64 * K);
+  float* sRed = sSa + 64 * nkb;
+
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+
+  // phase 1: A block and its scales into LDS, K-block-major: sA[kb][row][128 bytes]
+  // (16-byte chunks XOR-swizzled by row) and sSa[kb][row]. One direct-to-LDS instruction
+  // fills 1 KB (lane i -> bytes 16i..16i+15) = 8 rows of one K block; each lane fetches
+  // the global chunk that belongs at its LDS position.
+  {
+    const int nchunk = nkb * 512;  // 64 rows x 8 chunks per K block
+    for (int c0 = w * 64; c0 < nchunk; c0 += 64 * NW) {
+      const int c = c0 + l;
+      const int kb = c >> 9, row = (c >> 3) & 63, ch = c & 7;
+      const uint8_t* src = A + clamp_rows(m0 + row, valid - 1) * K + kb * kQ + ((ch ^ (row & 7)) << 4);
+      __builtin_amdgcn_global_load_lds(src, sA + (uint32_t)c0 * 16, 16, 0, 0);
+    }
+    for (int i = t; i < 64 * nkb; i += 64 * NW) {
+      const int kb = i >> 6, row = i & 63;
+      sSa[i] = SA[clamp_rows(m0 + row, valid - 1) * nkb + kb];
+    }
+  }
+
+  const int slot = w / KSPLIT, kpart = w % KSPLIT;
+  const int fr = l & 15;
+  const int g4 = l >> 4;
+  const int kof = g4 * 16;
+  // swizzled positions of this lane's two 16-byte chunks (g4 and g4+4) in its row
+  const int sw0 = (g4 ^ (fr & 7)) << 4, sw1 = ((g4 + 4) ^ (fr & 7)) << 4;
+
+  // all weight fragments of this wave's K blocks for the unit of round `ub`
+  auto issue = [&](v8i (&bf)[KW][TN], float (&sbv)[KW], int ub) {
+    const int u = min(ub + slot, u1 - 1);
+    const int64_t n0 = (int64_t)u * UW;
+    const uint8_t* bp = B + (n0 + fr) * K + kof;  // this lane's row of the unit
+    const float* SB = SBg + (n0 / kQ) * nkb;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      const int kb = kpart + KSPLIT * i;
+      const int kc = min(kb, nkb - 1);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[i][j] = load_frag_global(bp + (uint32_t)(16 * j * (int)K + kc * kQ));
+      sbv[i] = SB[kc] * (kb < nkb ? 1.0f : 0.0f);
+    }
+  };
+
+  auto consume = [&](v8i (&bf)[KW][TN], float (&sbv)[KW], int ub) {
+    const int u = ub + slot;
+    const bool active = u < u1;
+    const int64_t n0 = (int64_t)min(u, u1 - 1) * UW;
+    v4f acc[4][TN];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      const int kb = kpart + KSPLIT * i;
+      const int kc = min(kb, nkb - 1);
+      const uint8_t* ablk = sA + kc * 8192 + fr * 128;
+      const float* sblk = sSa + kc * 64 + 4 * g4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v8i af = cat8(*reinterpret_cast<const v4i*>(ablk + s * 2048 + sw0),
+                            *reinterpret_cast<const v4i*>(ablk + s * 2048 + sw1));
+        const float4 s4 = *reinterpret_cast<const float4*>(sblk + 16 * s);
+        const float t0 = s4.x * sbv[i], t1 = s4.y * sbv[i], t2 = s4.z * sbv[i], t3 = s4.w * sbv[i];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const v4f pp = mfma_f8_16x16x128(af, bf[i][j]);
+          acc[s][j][0] = fmaf(pp[0], t0, acc[s][j][0]);
+          acc[s][j][1] = fmaf(pp[1], t1, acc[s][j][1]);
+          acc[s][j][2] = fmaf(pp[2], t2, acc[s][j][2]);
+          acc[s][j][3] = fmaf(pp[3], t3, acc[s][j][3]);
+        }
+      }
+      // keep the scheduler from hoisting every K block's LDS reads (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (KSPLIT > 1) {
+      // partial tiles of K parts 1.. go through LDS to the K-part-0 wave of the slot
+      if (kpart > 0) {
+        float* dst = sRed + ((slot * (KSPLIT - 1) + (kpart - 1)) * 64) * UW;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(16 * s + 4 * g4 + r) * UW + 16 * j + fr] = acc[s][j][r];
+      }
+      lds_barrier();
+      if (kpart == 0) {
+#pragma unroll
+        for (int q = 1; q < KSPLIT; ++q) {
+          const float* src = sRed + ((slot * (KSPLIT - 1) + (q - 1)) * 64) * UW;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[s][j][r] += src[(16 * s + 4 * g4 + r) * UW + 16 * j + fr];
+        }
+      }
+    }
+    if (kpart == 0 && active) {
+      uint16_t* dbase = D + (m0 + 4 * g4) * p.N + n0 + fr;
+      const int rows_left = (int)(valid - m0 - 4 * g4);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (16 * s + r < rows_left) {
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              dbase[(uint32_t)((16 * s + r) * (int)p.N + 16 * j)] = (uint16_t)bf16_rne(acc[s][j][r]);
+          }
+        }
+      }
+    }
+    if constexpr (KSPLIT > 1) lds_barrier();  // the partial slots are reused next round
+  };
+
+  if (u0 >= u1) {  // no columns for this workgroup: drain the LDS loads and leave
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+  // rounds of SLOTS units; the next round's weights load while this round computes
+  v8i bfa[KW][TN], bfb[KW][TN];
+  float sba[KW], sbb[KW];
+  issue(bfa, sba, u0);
+  __builtin_amdgcn_s_waitcnt(0);  // the A block (direct-to-LDS) has landed, in every wave
+  __syncthreads();
+  for (int ub = u0;;) {
+    if (ub + SLOTS >= u1) { consume(bfa, sba, ub); break; }
+    issue(bfb, sbb, ub + SLOTS);
+    consume(bfa, sba, ub);
+    ub += SLOTS;
+    if (ub + SLOTS >= u1) { consume(bfb, sbb, ub); break; }
+    issue(bfa, sba, ub + SLOTS);
+    consume(bfb, sbb, ub);
+    ub += SLOTS;
   }
 }
 
@@ -270,9 +458,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // fragment read offsets (swizzled 16-byte columns 2*(l>>4) and 2*(l>>4)+1)
+  // fragment read offsets: 16-byte columns (l>>4) and 4+(l>>4) of the row, swizzled
   const int fr = l & 15;
-  const int c0 = 2 * (l >> 4), c1 = c0 + 1;
+  const int c0 = l >> 4, c1 = c0 + 4;
 
   gload(0);
   lstore(0);
@@ -332,7 +520,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
   }
 }
 
-template <int BN, int NW, Layout L>
+template <int BN, int NW, int KPW, Layout L>
 hipError_t run_decode(KParams kp, hipStream_t s) {
   kp.tiles_n = (int)(kp.N / BN);
   kp.tiles_m = (int)((kp.M + 63) / 64);
@@ -340,7 +528,7 @@ hipError_t run_decode(KParams kp, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
-  gemm_decode_kernel<BN, NW, L><<<dim3((unsigned)nwg), dim3(64 * NW), 0, s>>>(kp);
+  gemm_decode_kernel<BN, NW, KPW, L><<<dim3((unsigned)nwg), dim3(64 * NW), 0, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -356,22 +544,151 @@ hipError_t run_tile(KParams kp, hipStream_t s) {
   return hipGetLastError();
 }
 
+constexpr size_t kLdsBytes = 163840;  // gfx950 LDS per workgroup
+
+template <int TN, int KSPLIT, int NW, int KW>
+constexpr size_t decode_lds_bytes(int64_t K, int nkb) {
+  return (size_t)(64 * K) + (size_t)4 * 64 * nkb + (size_t)(NW / KSPLIT) * (KSPLIT - 1) * 64 * 16 * TN * 4;
+}
+
+template <int TN, int KSPLIT, int NW, int KW, Layout L>
+hipError_t run_decode_lds(KParams kp, int parts, hipStream_t s) {
+  const size_t lds = decode_lds_bytes<TN, KSPLIT, NW, KW>(kp.K, kp.nkb);
+  if (lds > kLdsBytes || (int64_t)KSPLIT * KW < kp.nkb || parts < 1) return hipErrorInvalidValue;
+  kp.tiles_m = (int)((kp.M + 63) / 64);
+  kp.tiles_n = parts;
+  const int64_t nwg = (int64_t)kp.G * kp.tiles_m * parts;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
+  return hipGetLastError();
+}
+
+// Instantiated configurations of the LDS-resident decode schedule:
+// (columns/16 per unit, waves per unit, waves, K blocks per wave).
+#define DG_DECODE_LDS_CONFIGS(X) \
+  X(1, 4, 8, 4) X(1, 4, 8, 3) X(1, 4, 8, 2) X(1, 2, 8, 4) X(1, 8, 8, 2) X(1, 2, 8, 2)
+
+struct DecodeLdsCfg { int tn, ksplit, nw, kw; };
+
+template <Layout L>
+hipError_t run_decode_lds_cfg(const DecodeLdsCfg& c, int parts, const KParams& kp, hipStream_t s, bool* found) {
+  *found = true;
+#define DG_X(a, b, c_, d) \
+  if (c.tn == a && c.ksplit == b && c.nw == c_ && c.kw == d) return run_decode_lds<a, b, c_, d, L>(kp, parts, s);
+  DG_DECODE_LDS_CONFIGS(DG_X)
+#undef DG_X
+  *found = false;
+  return hipSuccess;
+}
+
+size_t decode_lds_need(const DecodeLdsCfg& c, int64_t K, int nkb) {
+  return (size_t)(64 * K) + (size_t)4 * 64 * nkb + (size_t)(c.nw / c.ksplit) * (c.ksplit - 1) * 64 * 16 * c.tn * 4;
+}
+
+// Picks an LDS-resident decode configuration, or returns false when none fits.
+template <Layout L>
+bool try_decode_lds(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
+  static thread_local char name[80];
+  const int nkb = kp.nkb;
+  if (kp.N * 64 >= ((int64_t)1 << 31)) return false;  // 32-bit output offsets
+  DecodeLdsCfg c{0, 0, 0, 0};
+  int parts = 0;
+  const char* env = getenv("DG_DECODE_LDS");
+  if (env && sscanf(env, "%d,%d,%d,%d,%d", &c.tn, &c.ksplit, &c.nw, &c.kw, &parts) == 5) {
+    // tuning override
+  } else {
+    static const DecodeLdsCfg prefs[] = {{1, 2, 8, 2}, {1, 4, 8, 2}, {1, 2, 8, 4}, {1, 4, 8, 3}, {1, 4, 8, 4},
+                                         {1, 8, 8, 2}};
+    const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
+    bool got = false;
+    for (const DecodeLdsCfg& q : prefs) {
+      if ((int64_t)q.ksplit * q.kw < nkb || decode_lds_need(q, kp.K, nkb) > kLdsBytes) continue;
+      const int64_t units = kp.N / (16 * q.tn);
+      const int slots = q.nw / q.ksplit;
+      // at most one round per workgroup and enough workgroups to cover the CUs
+      const int64_t p1 = (units + slots - 1) / slots;
+      if (p1 * rowblocks < 200) continue;
+      c = q;
+      parts = (int)(p1 * rowblocks > 512 ? (512 + rowblocks - 1) / rowblocks : p1);
+      got = true;
+      break;
+    }
+    if (!got) return false;
+  }
+  if (decode_lds_need(c, kp.K, nkb) > kLdsBytes || (int64_t)c.ksplit * c.kw < nkb) return false;
+  bool found = false;
+  *err = run_decode_lds_cfg<L>(c, parts, kp, s, &found);
+  if (!found) return false;
+  snprintf(name, sizeof name, "decode_lds_tn%d_ks%d_w%d_kw%d_p%d", c.tn, c.ksplit, c.nw, c.kw, parts);
+  if (chosen) *chosen = name;
+  return true;
+}
+
+// Instantiated decode configurations: (columns per workgroup, waves, K blocks per wave
+// per round).
+#define DG_DECODE_CONFIGS(X) \
+  X(16, 8, 2) X(16, 4, 3) X(16, 4, 4) X(16, 6, 2) X(16, 12, 1) X(16, 8, 1) \
+  X(32, 4, 3) X(32, 8, 2) X(32, 4, 4) X(32, 6, 2) X(32, 12, 1) X(32, 8, 1) \
+  X(64, 8, 2) X(64, 4, 3) X(64, 4, 4)
+
+template <Layout L>
+hipError_t run_decode_cfg(int bn, int nw, int kpw, const KParams& kp, hipStream_t s, bool* found) {
+  *found = true;
+#define DG_X(a, b, c) \
+  if (bn == a && nw == b && kpw == c) return run_decode<a, b, c, L>(kp, s);
+  DG_DECODE_CONFIGS(DG_X)
+#undef DG_X
+  *found = false;
+  return hipSuccess;
+}
+
 template <Layout L>
 hipError_t run_decode_auto(const KParams& kp, hipStream_t s, const char** chosen) {
-  // Enough workgroups to cover the 256 CUs twice: prefer the widest column tile that
-  // still yields >= 512 workgroups; split K over 8 waves when there are >= 16 K blocks.
-  const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
-  const bool eight = kp.nkb >= 16;
-  if (rowblocks * (kp.N / 64) >= 512) {
-    if (chosen) *chosen = eight ? "decode_bn64_w8" : "decode_bn64_w4";
-    return eight ? run_decode<64, 8, L>(kp, s) : run_decode<64, 4, L>(kp, s);
+  static thread_local char name[64];
+  if (getenv("DG_DECODE_LDS")) {  // tuning: the LDS-resident variant
+    hipError_t e = hipSuccess;
+    if (try_decode_lds<L>(kp, s, chosen, &e)) return e;
   }
-  if (rowblocks * (kp.N / 32) >= 512) {
-    if (chosen) *chosen = eight ? "decode_bn32_w8" : "decode_bn32_w4";
-    return eight ? run_decode<32, 8, L>(kp, s) : run_decode<32, 4, L>(kp, s);
+  int bn = 32, nw = 8, kpw = 2;
+  // DG_DECODE_CFG="bn,nw,kpw" overrides the choice (tuning); unknown triples are ignored.
+  const char* env = getenv("DG_DECODE_CFG");
+  bool forced = false;
+  if (env && sscanf(env, "%d,%d,%d", &bn, &nw, &kpw) == 3) forced = true;
+  if (!forced) {
+    // One round per wave (all K blocks of a wave in flight at once) and at least ~448
+    // workgroups for the 256 CUs; prefer wider column tiles (less A re-reading).
+    const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
+    const int nkb = kp.nkb;
+    struct C { int bn, nw, kpw; };
+    // measured on MI355X (rocprofv3): nkb 12 -> (32,4,3), nkb 16 -> (32,8,2) or (32,12,1)
+    static const C prefs[] = {{32, 4, 3}, {32, 8, 2}, {32, 4, 4}, {16, 8, 2}, {16, 4, 3}, {16, 4, 4}};
+    bool got = false;
+    for (const C& c : prefs) {
+      if (c.nw * c.kpw < nkb) continue;
+      if (rowblocks * (kp.N / c.bn) < 448) continue;
+      bn = c.bn; nw = c.nw; kpw = c.kpw; got = true;
+      break;
+    }
+    if (!got) {
+      if (rowblocks * (kp.N / 32) >= 448) { bn = 32; nw = 8; kpw = 2; }
+      else { bn = 16; nw = 8; kpw = 2; }
+    }
   }
-  if (chosen) *chosen = eight ? "decode_bn16_w8" : "decode_bn16_w4";
-  return eight ? run_decode<16, 8, L>(kp, s) : run_decode<16, 4, L>(kp, s);
+  bool found = false;
+  hipError_t e = run_decode_cfg<L>(bn, nw, kpw, kp, s, &found);
+  if (!found) {
+    bn = 32; nw = 8; kpw = 2;
+    e = run_decode_cfg<L>(bn, nw, kpw, kp, s, &found);
+  }
+  snprintf(name, sizeof name, "decode_bn%d_w%d_k%d", bn, nw, kpw);
+  if (chosen) *chosen = name;
+  return e;
 }
 
 }  // namespace
