@@ -532,6 +532,216 @@ hipError_t run_decode(KParams kp, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// tile schedule, deep prefetch
+// ---------------------------------------------------------------------------------
+// BM x BN workgroup tile, (WM x WN) waves of (BM/WM) x (BN/WN). Global loads run two K
+// blocks ahead of the MFMAs through two register staging sets; each K block is written
+// to one of two LDS buffers and read back as MFMA fragments. Barriers order LDS only, so
+// the loads for the next two K blocks stay in flight across them.
+template <int BM, int BN, int WM, int WN, Layout L>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int ACH = BM * 8 / NT;  // 16-byte chunks of an A K-block per thread
+  constexpr int BCH = BN * 8 / NT;
+  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "chunk split");
+  static_assert(kQ % BN == 0, "tile must sit inside one weight-scale block column");
+  static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
+  static_assert(BM <= NT, "one activation scale per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kQ];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kQ];
+  __shared__ __attribute__((aligned(16))) float sSa[2][BM];
+
+  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
+  int g = 0, tm, tn;
+  if constexpr (L == Layout::Masked) {
+    tm = (int)(wg % (uint32_t)p.tiles_m);
+    tn = (int)((wg / (uint32_t)p.tiles_m) % (uint32_t)p.tiles_n);
+    g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  } else {
+    constexpr int GM = 8;
+    const int per_band = GM * p.tiles_n;
+    const int band = (int)wg / per_band;
+    const int first = band * GM;
+    const int gm = min(p.tiles_m - first, GM);
+    const int in = (int)wg % per_band;
+    tm = first + in % gm;
+    tn = in / gm;
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  int64_t valid = p.M;
+  if constexpr (L == Layout::Masked) {
+    valid = clamp_rows(p.masked_m[g], p.M);
+    if (m0 >= valid) return;
+  }
+  if constexpr (L == Layout::Contiguous) {
+    g = p.m_indices[m0];
+    if (g < 0 || g >= p.G) return;
+  }
+  const int nkb = p.nkb;
+  const int64_t K = p.K;
+  const uint8_t* A = p.a + (L == Layout::Masked ? (int64_t)g * p.M * K : 0);
+  const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0);
+  const uint8_t* B = p.b + (int64_t)g * p.N * K;
+  const float* SB = p.sfb + ((int64_t)g * (p.N / kQ) + n0 / kQ) * nkb;
+  uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
+
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int wm = w % WM, wn = w / WM;
+
+  // staging: chunk c = t + NT*u is row c/8, 16-byte column c%8 (rows read whole)
+  const uint8_t* ga = A + clamp_rows(m0 + (t >> 3), valid - 1) * K + (t & 7) * 16;
+  const uint8_t* gb = B + (n0 + (t >> 3)) * K + (t & 7) * 16;
+  constexpr int RSTEP = NT / 8;  // rows advanced per staging step
+  const uint32_t lst = (uint32_t)((t >> 3) * kQ + (((t & 7) ^ ((t >> 3) & 7)) << 4));
+  // every thread loads and stores an activation scale (threads t and t+BM duplicate one
+  // row): no divergent branch inside the pipelined loop
+  const int srow = t % BM;
+  const float* gsa = SA + clamp_rows(m0 + srow, valid - 1) * nkb;
+  // A rows beyond the valid count are clamped to the last valid row (per staging step)
+  int64_t arow_off[ACH];
+#pragma unroll
+  for (int u = 0; u < ACH; ++u) {
+    const int64_t r = m0 + (t >> 3) + RSTEP * u;
+    arow_off[u] = (clamp_rows(r, valid - 1) - clamp_rows(m0 + (t >> 3), valid - 1)) * K;
+  }
+
+  v4i ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
+  float rs0 = 0.f, rs1 = 0.f;
+  auto gload = [&](v4i (&ra)[ACH], v4i (&rb)[BCH], float& rs, int kb) {
+    const uint32_t ko = (uint32_t)kb * kQ;
+#pragma unroll
+    for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga + arow_off[u] + ko);
+#pragma unroll
+    for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb + (int64_t)RSTEP * u * K + ko);
+    rs = gsa[kb];
+  };
+  auto lstore = [&](const v4i (&ra)[ACH], const v4i (&rb)[BCH], float rs, int buf) {
+#pragma unroll
+    for (int u = 0; u < ACH; ++u) *reinterpret_cast<v4i*>(&sA[buf][lst + RSTEP * u * kQ]) = ra[u];
+#pragma unroll
+    for (int u = 0; u < BCH; ++u) *reinterpret_cast<v4i*>(&sB[buf][lst + RSTEP * u * kQ]) = rb[u];
+    sSa[buf][srow] = rs;
+  };
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = l & 15, g4 = l >> 4;
+  const uint32_t sw0 = (uint32_t)((g4 ^ (fr & 7)) << 4), sw1 = (uint32_t)(((g4 + 4) ^ (fr & 7)) << 4);
+  const uint32_t a_lane = (uint32_t)((wm * WTM + fr) * kQ), b_lane = (uint32_t)((wn * WTN + fr) * kQ);
+  const int sa_lane = wm * WTM + 4 * g4;
+
+  // One K block: TM x TN MFMAs, each promoted with one FMA per output element. The
+  // promotion of strip i-1 is interleaved with the MFMAs of strip i (software pipeline),
+  // so the matrix pipe never waits on the FMAs that consume its previous results.
+  auto compute = [&](int buf, float sb) {
+    const uint8_t* a_s = sA[buf] + a_lane;
+    const uint8_t* b_s = sB[buf] + b_lane;
+    v8i bfr[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bfr[j] = cat8(*reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw0),
+                    *reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw1));
+    v4f pp[2][TN];
+    float tt[2][4];
+#pragma unroll
+    for (int i = 0; i <= TM; ++i) {
+      const int cur = i & 1, prv = cur ^ 1;
+      if (i < TM) {
+        const v8i afr = cat8(*reinterpret_cast<const v4i*>(a_s + i * 16 * kQ + sw0),
+                             *reinterpret_cast<const v4i*>(a_s + i * 16 * kQ + sw1));
+        const float4 s4 = *reinterpret_cast<const float4*>(&sSa[buf][sa_lane + 16 * i]);
+        tt[cur][0] = s4.x * sb; tt[cur][1] = s4.y * sb; tt[cur][2] = s4.z * sb; tt[cur][3] = s4.w * sb;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) pp[cur][j] = mfma_f8_16x16x128(afr, bfr[j]);
+      }
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i - 1][j][0] = fmaf(pp[prv][j][0], tt[prv][0], acc[i - 1][j][0]);
+          acc[i - 1][j][1] = fmaf(pp[prv][j][1], tt[prv][1], acc[i - 1][j][1]);
+          acc[i - 1][j][2] = fmaf(pp[prv][j][2], tt[prv][2], acc[i - 1][j][2]);
+          acc[i - 1][j][3] = fmaf(pp[prv][j][3], tt[prv][3], acc[i - 1][j][3]);
+        }
+      }
+      if (i > 0 && i < TM) {
+        // scheduling hint: alternate one MFMA with the four FMAs of an earlier result
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+    }
+  };
+
+  // prologue: K block 0 into LDS buffer 0, K block 1 in flight in set 1
+  gload(ra0, rb0, rs0, 0);
+  gload(ra1, rb1, rs1, min(1, nkb - 1));
+  lstore(ra0, rb0, rs0, 0);
+  lds_barrier();
+  // steady state: two K blocks per trip, straight-line so that each LDS store waits only
+  // for its own staging set while the other set's loads stay in flight
+  int kb = 0;
+  for (; kb + 3 < nkb; kb += 2) {
+    const float sb0 = SB[kb], sb1 = SB[kb + 1];
+    gload(ra0, rb0, rs0, kb + 2);
+    compute(0, sb0);
+    lstore(ra1, rb1, rs1, 1);
+    lds_barrier();
+    gload(ra1, rb1, rs1, kb + 3);
+    compute(1, sb1);
+    lstore(ra0, rb0, rs0, 0);
+    lds_barrier();
+  }
+  // tail: 1 to 3 K blocks left; buffer 0 holds kb, set 1 holds kb + 1
+  if (kb + 2 < nkb) gload(ra0, rb0, rs0, kb + 2);
+  compute(0, SB[kb]);
+  if (kb + 1 < nkb) {
+    lstore(ra1, rb1, rs1, 1);
+    lds_barrier();
+    compute(1, SB[kb + 1]);
+    if (kb + 2 < nkb) {
+      lstore(ra0, rb0, rs0, 0);
+      lds_barrier();
+      compute(0, SB[kb + 2]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm * WTM + 16 * i + 4 * g4 + r;
+      if (row < valid) {
+        uint16_t* drow = D + row * p.N + n0 + wn * WTN + fr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) drow[16 * j] = (uint16_t)bf16_rne(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, Layout L>
+hipError_t run_tile2(KParams kp, hipStream_t s) {
+  kp.tiles_n = (int)(kp.N / BN);
+  kp.tiles_m = (int)((kp.M + BM - 1) / BM);
+  const int64_t nwg = (int64_t)(L == Layout::Masked ? kp.G : 1) * kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  gemm_tile2_kernel<BM, BN, WM, WN, L><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, Layout L>
 hipError_t run_tile(KParams kp, hipStream_t s) {
   kp.tiles_n = (int)(kp.N / BN);
@@ -710,26 +920,33 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   }
   if (p.layout == Layout::Contiguous && sched != Schedule::Tile128) sched = Schedule::Tile128;
 
+  // DG_TILE_V1=1 selects the single-stage tile kernel (for comparison while tuning)
+  const bool v1 = getenv("DG_TILE_V1") != nullptr;
   switch (p.layout) {
     case Layout::Dense:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Dense>(kp, stream, chosen);
       if (sched == Schedule::Tile256) {
-        if (chosen) *chosen = "tile_256x128";
-        return run_tile<256, 128, 4, 2, Layout::Dense>(kp, stream);
+        if (chosen) *chosen = v1 ? "tile_v1_256x128" : "tile_256x128";
+        return v1 ? run_tile<256, 128, 4, 2, Layout::Dense>(kp, stream)
+                  : run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
       }
-      if (chosen) *chosen = "tile_128x128";
-      return run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream);
+      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
+      return v1 ? run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream)
+                : run_tile2<128, 128, 2, 2, Layout::Dense>(kp, stream);
     case Layout::Masked:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Masked>(kp, stream, chosen);
       if (sched == Schedule::Tile256) {
-        if (chosen) *chosen = "tile_256x128";
-        return run_tile<256, 128, 4, 2, Layout::Masked>(kp, stream);
+        if (chosen) *chosen = v1 ? "tile_v1_256x128" : "tile_256x128";
+        return v1 ? run_tile<256, 128, 4, 2, Layout::Masked>(kp, stream)
+                  : run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
       }
-      if (chosen) *chosen = "tile_128x128";
-      return run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream);
+      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
+      return v1 ? run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream)
+                : run_tile2<128, 128, 2, 2, Layout::Masked>(kp, stream);
     case Layout::Contiguous:
-      if (chosen) *chosen = "tile_128x128";
-      return run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
+      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
+      return v1 ? run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream)
+                : run_tile2<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
   }
   return hipErrorInvalidValue;
 }
