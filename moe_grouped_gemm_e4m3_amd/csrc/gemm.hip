@@ -547,12 +547,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   constexpr int ACH = BM * 8 / NT;  // 16-byte chunks of an A K-block per thread
   constexpr int BCH = BN * 8 / NT;
   static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "chunk split");
-  static_assert(kQ % BN == 0, "tile must sit inside one weight-scale block column");
+  // weight-scale column blocks per tile; each wave's columns lie inside one of them
+  constexpr int NB = BN > (int)kQ ? BN / (int)kQ : 1;
+  static_assert((BN % kQ == 0 || kQ % BN == 0) && kQ % WTN == 0, "tile vs weight-scale blocks");
   static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
   static_assert(BM <= NT, "one activation scale per thread");
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kQ];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kQ];
-  __shared__ __attribute__((aligned(16))) float sSa[2][BM];
+  __shared__ __attribute__((aligned(16))) float sSa[2][NB][BM];
 
   const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
   int g = 0, tm, tn;
@@ -600,30 +602,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   // row): no divergent branch inside the pipelined loop
   const int srow = t % BM;
   const float* gsa = SA + clamp_rows(m0 + srow, valid - 1) * nkb;
-  // A rows beyond the valid count are clamped to the last valid row (per staging step)
-  int64_t arow_off[ACH];
+  // byte offsets of the staged A rows from the first one (rows past the valid count are
+  // clamped to the last valid row); B rows are always in range
+  uint32_t aoff[ACH];
 #pragma unroll
   for (int u = 0; u < ACH; ++u) {
     const int64_t r = m0 + (t >> 3) + RSTEP * u;
-    arow_off[u] = (clamp_rows(r, valid - 1) - clamp_rows(m0 + (t >> 3), valid - 1)) * K;
+    aoff[u] = (uint32_t)((clamp_rows(r, valid - 1) - clamp_rows(m0 + (t >> 3), valid - 1)) * K);
   }
+  const uint32_t bstep = (uint32_t)(RSTEP * K);
 
   v4i ra0[ACH], rb0[BCH], ra1[ACH], rb1[BCH];
-  float rs0 = 0.f, rs1 = 0.f;
-  auto gload = [&](v4i (&ra)[ACH], v4i (&rb)[BCH], float& rs, int kb) {
+  float rs0[NB], rs1[NB];
+  // loads one K block; the activation scale is multiplied by the K block's weight scale
+  // here, so LDS holds the full promotion factor sa[m,kb] * sb[n/128,kb]
+  auto gload = [&](v4i (&ra)[ACH], v4i (&rb)[BCH], float (&rs)[NB], int kb) {
     const uint32_t ko = (uint32_t)kb * kQ;
 #pragma unroll
-    for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga + arow_off[u] + ko);
+    for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga + aoff[u] + ko);
 #pragma unroll
-    for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb + (int64_t)RSTEP * u * K + ko);
-    rs = gsa[kb];
+    for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb + bstep * u + ko);
+    const float sa = gsa[kb];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) rs[nb] = sa * SB[nb * nkb + kb];
   };
-  auto lstore = [&](const v4i (&ra)[ACH], const v4i (&rb)[BCH], float rs, int buf) {
+  auto lstore = [&](const v4i (&ra)[ACH], const v4i (&rb)[BCH], const float (&rs)[NB], int buf) {
 #pragma unroll
     for (int u = 0; u < ACH; ++u) *reinterpret_cast<v4i*>(&sA[buf][lst + RSTEP * u * kQ]) = ra[u];
 #pragma unroll
     for (int u = 0; u < BCH; ++u) *reinterpret_cast<v4i*>(&sB[buf][lst + RSTEP * u * kQ]) = rb[u];
-    sSa[buf][srow] = rs;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) sSa[buf][nb][srow] = rs[nb];
   };
 
   v4f acc[TM][TN];
@@ -640,43 +649,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   // One K block: TM x TN MFMAs, each promoted with one FMA per output element. The
   // promotion of strip i-1 is interleaved with the MFMAs of strip i (software pipeline),
   // so the matrix pipe never waits on the FMAs that consume its previous results.
-  auto compute = [&](int buf, float sb) {
+  // MFMA products and promotion factors of the two most recent strips. The promotion of
+  // a strip runs under the MFMAs of the next one, also across K blocks: the last strip of
+  // a K block is promoted under the first MFMAs of the next K block. The slots start at
+  // zero, so the first promotion adds 0 * 0.
+  static_assert(TM % 2 == 0, "strip parity must repeat every K block");
+  v4f pp[2][TN];
+  float4 tt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    tt[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pp[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  auto promote = [&](int slot, int strip) {
+    const float4 tp = tt[slot];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      acc[strip][j][0] = fmaf(pp[slot][j][0], tp.x, acc[strip][j][0]);
+      acc[strip][j][1] = fmaf(pp[slot][j][1], tp.y, acc[strip][j][1]);
+      acc[strip][j][2] = fmaf(pp[slot][j][2], tp.z, acc[strip][j][2]);
+      acc[strip][j][3] = fmaf(pp[slot][j][3], tp.w, acc[strip][j][3]);
+    }
+  };
+  auto compute = [&](int buf) {
     const uint8_t* a_s = sA[buf] + a_lane;
     const uint8_t* b_s = sB[buf] + b_lane;
+    const float* t_s = &sSa[buf][(wn * WTN) / (int)kQ][sa_lane];
     v8i bfr[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       bfr[j] = cat8(*reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw0),
                     *reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw1));
-    v4f pp[2][TN];
-    float tt[2][4];
+    v8i afr[2];
+    float4 tn[2];
+    afr[0] = cat8(*reinterpret_cast<const v4i*>(a_s + sw0), *reinterpret_cast<const v4i*>(a_s + sw1));
+    tn[0] = *reinterpret_cast<const float4*>(t_s);
 #pragma unroll
-    for (int i = 0; i <= TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
       const int cur = i & 1, prv = cur ^ 1;
-      if (i < TM) {
-        const v8i afr = cat8(*reinterpret_cast<const v4i*>(a_s + i * 16 * kQ + sw0),
-                             *reinterpret_cast<const v4i*>(a_s + i * 16 * kQ + sw1));
-        const float4 s4 = *reinterpret_cast<const float4*>(&sSa[buf][sa_lane + 16 * i]);
-        tt[cur][0] = s4.x * sb; tt[cur][1] = s4.y * sb; tt[cur][2] = s4.z * sb; tt[cur][3] = s4.w * sb;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) pp[cur][j] = mfma_f8_16x16x128(afr, bfr[j]);
+      if (i + 1 < TM) {  // next strip's fragment and factors, one strip ahead
+        afr[prv] = cat8(*reinterpret_cast<const v4i*>(a_s + (i + 1) * 16 * kQ + sw0),
+                        *reinterpret_cast<const v4i*>(a_s + (i + 1) * 16 * kQ + sw1));
+        tn[prv] = *reinterpret_cast<const float4*>(t_s + 16 * (i + 1));
       }
-      if (i > 0) {
+      // MFMAs of strip i into slot cur; promotion of the previous strip from slot prv
+      v4f fresh[TN];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i - 1][j][0] = fmaf(pp[prv][j][0], tt[prv][0], acc[i - 1][j][0]);
-          acc[i - 1][j][1] = fmaf(pp[prv][j][1], tt[prv][1], acc[i - 1][j][1]);
-          acc[i - 1][j][2] = fmaf(pp[prv][j][2], tt[prv][2], acc[i - 1][j][2]);
-          acc[i - 1][j][3] = fmaf(pp[prv][j][3], tt[prv][3], acc[i - 1][j][3]);
-        }
-      }
-      if (i > 0 && i < TM) {
-        // scheduling hint: alternate one MFMA with the four FMAs of an earlier result
+      for (int j = 0; j < TN; ++j) fresh[j] = mfma_f8_16x16x128(afr[cur], bfr[j]);
+      promote(prv, i > 0 ? i - 1 : TM - 1);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-        }
+      for (int j = 0; j < TN; ++j) pp[cur][j] = fresh[j];
+      tt[cur] = tn[cur];
+      // scheduling hint: alternate one MFMA with four promotion FMAs
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
     }
   };
@@ -690,29 +719,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   // for its own staging set while the other set's loads stay in flight
   int kb = 0;
   for (; kb + 3 < nkb; kb += 2) {
-    const float sb0 = SB[kb], sb1 = SB[kb + 1];
     gload(ra0, rb0, rs0, kb + 2);
-    compute(0, sb0);
+    compute(0);
     lstore(ra1, rb1, rs1, 1);
     lds_barrier();
     gload(ra1, rb1, rs1, kb + 3);
-    compute(1, sb1);
+    compute(1);
     lstore(ra0, rb0, rs0, 0);
     lds_barrier();
   }
   // tail: 1 to 3 K blocks left; buffer 0 holds kb, set 1 holds kb + 1
   if (kb + 2 < nkb) gload(ra0, rb0, rs0, kb + 2);
-  compute(0, SB[kb]);
+  compute(0);
   if (kb + 1 < nkb) {
     lstore(ra1, rb1, rs1, 1);
     lds_barrier();
-    compute(1, SB[kb + 1]);
+    compute(1);
     if (kb + 2 < nkb) {
       lstore(ra0, rb0, rs0, 0);
       lds_barrier();
-      compute(0, SB[kb + 2]);
+      compute(0);
     }
   }
+  promote(1, TM - 1);  // the last strip (odd slot, TM even)
   __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
@@ -912,41 +941,59 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
 
   if (sched == Schedule::Auto) {
     if (p.layout == Layout::Dense)
-      sched = p.M <= 64 ? Schedule::Decode : Schedule::Tile128;
+      sched = p.M <= 64 ? Schedule::Decode : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
     else if (p.layout == Layout::Masked)
-      sched = (expected_m > 0 && expected_m <= 64) ? Schedule::Decode : Schedule::Tile128;
+      sched = (expected_m > 0 && expected_m <= 64) ? Schedule::Decode : Schedule::Tile256;
     else
       sched = Schedule::Tile128;
   }
   if (p.layout == Layout::Contiguous && sched != Schedule::Tile128) sched = Schedule::Tile128;
 
-  // DG_TILE_V1=1 selects the single-stage tile kernel (for comparison while tuning)
+  // DG_TILE_V1=1 selects the single-stage tile kernel (for comparison while tuning);
+  // DG_TILE_SHAPE=BMxBN forces one of the instantiated deep-prefetch tiles.
   const bool v1 = getenv("DG_TILE_V1") != nullptr;
+  int fbm = 0, fbn = 0;
+  if (const char* e = getenv("DG_TILE_SHAPE")) sscanf(e, "%dx%d", &fbm, &fbn);
   switch (p.layout) {
     case Layout::Dense:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Dense>(kp, stream, chosen);
-      if (sched == Schedule::Tile256) {
-        if (chosen) *chosen = v1 ? "tile_v1_256x128" : "tile_256x128";
-        return v1 ? run_tile<256, 128, 4, 2, Layout::Dense>(kp, stream)
-                  : run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
+      if (v1) {
+        if (chosen) *chosen = "tile_v1_128x128";
+        return run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream);
       }
-      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
-      return v1 ? run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream)
-                : run_tile2<128, 128, 2, 2, Layout::Dense>(kp, stream);
+      if (fbm == 128 && fbn == 256 && kp.N % 256 == 0) {
+        if (chosen) *chosen = "tile_128x256";
+        return run_tile2<128, 256, 2, 4, Layout::Dense>(kp, stream);
+      }
+      if (sched == Schedule::Tile256 || (fbm == 256 && fbn == 128)) {
+        if (chosen) *chosen = "tile_256x128";
+        return run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
+      }
+      if (chosen) *chosen = "tile_128x128";
+      return run_tile2<128, 128, 2, 4, Layout::Dense>(kp, stream);
     case Layout::Masked:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Masked>(kp, stream, chosen);
-      if (sched == Schedule::Tile256) {
-        if (chosen) *chosen = v1 ? "tile_v1_256x128" : "tile_256x128";
-        return v1 ? run_tile<256, 128, 4, 2, Layout::Masked>(kp, stream)
-                  : run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
+      if (v1) {
+        if (chosen) *chosen = "tile_v1_128x128";
+        return run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream);
       }
-      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
-      return v1 ? run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream)
-                : run_tile2<128, 128, 2, 2, Layout::Masked>(kp, stream);
+      if (sched == Schedule::Tile256) {
+        if (chosen) *chosen = "tile_256x128";
+        return run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
+      }
+      if (chosen) *chosen = "tile_128x128";
+      return run_tile2<128, 128, 2, 4, Layout::Masked>(kp, stream);
     case Layout::Contiguous:
-      if (chosen) *chosen = v1 ? "tile_v1_128x128" : "tile_128x128";
-      return v1 ? run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream)
-                : run_tile2<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
+      if (v1) {
+        if (chosen) *chosen = "tile_v1_128x128";
+        return run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
+      }
+      if (kp.N % 256 == 0 && !(fbm == 128 && fbn == 128)) {
+        if (chosen) *chosen = "tile_128x256";
+        return run_tile2<128, 256, 2, 4, Layout::Contiguous>(kp, stream);
+      }
+      if (chosen) *chosen = "tile_128x128";
+      return run_tile2<128, 128, 2, 4, Layout::Contiguous>(kp, stream);
   }
   return hipErrorInvalidValue;
 }
