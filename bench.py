@@ -6,17 +6,21 @@ layer's fp32 activations followed by its block-scaled FP8 GEMM (bf16 out), for b
 Inputs are resident in HBM before timing starts. Each step uses one of R copies of the
 weights (R * |weights| >= 512 MiB) so the 256 MiB Infinity Cache cannot serve them.
 
-Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included),
-`roofline` is for the kernel that takes the most time in the step, measured with HIP
-events on the launch stream over the timed region, and `cpu_baseline` is the CPU oracle
-on the host cores over a bounded sample of the same workload.
+Steps are captured in HIP graphs (one graph per weight copy, launched on torch's stream)
+and replayed, so the measurement is GPU time rather than Python launch overhead.
+
+Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included).
+`roofline` is for the kernel that takes the most time in the step; its average duration
+comes from HIP events around graphs of back-to-back launches of that kernel alone, on the
+stream it runs on. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
+of the same workload. `traffic` (HBM bytes per launch) is read from profiles/traffic.json
+when that file was produced from the current kernel source.
 
 Other workloads (--workload prefill|contiguous|masked|tiny) print the same line shape.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -117,19 +121,12 @@ def build_layer(dg, torch, kind, s, seed, copies):
     return dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G)
 
 
-def run_layer(dg, L, copy_idx, ev=None):
-    """Cast activations then GEMM; `ev` (list) receives (label, start, end) event pairs."""
-    import torch
+def run_layer(dg, L, copy_idx):
+    """Cast the layer's activations, then its GEMM with weight copy `copy_idx`."""
     kind, s = L["kind"], L["s"]
-    N, K = s["N"], s["K"]
+    K = s["K"]
     qb, sb = L["ws"][copy_idx % len(L["ws"])]
-    e = None
-    if ev is not None:
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
     dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"])
-    if ev is not None:
-        e[1].record()
     if kind == "dense":
         dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"])
     elif kind == "contiguous":
@@ -138,18 +135,6 @@ def run_layer(dg, L, copy_idx, ev=None):
         G, Mm = s["G"], s["M_max"]
         dg.grouped_gemm_masked(L["qa"].view(G, Mm, K), L["sa"].view(G, Mm, K // 128), qb, sb, L["meta"],
                                expected_m=max(1, L["valid"] // G), d=L["d"])
-    if ev is not None:
-        e[2].record()
-        ev.append(("cast", L, e[0], e[1]))
-        ev.append(("gemm", L, e[1], e[2]))
-
-
-def gemm_source_hash():
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "dg_device.h"):
-        with open(os.path.join(ROOT, "moe_grouped_gemm_e4m3_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def load_traffic(workload, label):
@@ -161,8 +146,9 @@ def load_traffic(workload, label):
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from moe_grouped_gemm_e4m3_amd.profiling import source_hash
     rec = t.get(workload, {}).get(label)
-    if not rec or rec.get("source_hash") != gemm_source_hash():
+    if not rec or rec.get("source_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -203,6 +189,34 @@ def cpu_baseline(workload, budget_s):
                       % (", ".join(sample_desc), reps, dt)}
 
 
+def capture(torch, fn):
+    """HIP graph of fn() on the current device (the binding launches on torch's current
+    stream, which is the capture stream inside torch.cuda.graph)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(torch, graphs, n):
+    """Replay graphs[i % len] for i < n between two events; returns ms."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,8 +226,12 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=0,
+                    help="launches per kernel in the per-kernel timing (default: steps)")
     ap.add_argument("--cache-bytes", type=float, default=512 * 2 ** 20,
                     help="minimum bytes of distinct weight copies cycled through")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see the sharding "
@@ -229,53 +247,75 @@ def main():
     torch.cuda.set_device(0)
 
     wl = WORKLOADS[args.workload]
-    # weight copies so each step streams its weights from HBM
+    # weight copies so each step streams its weights from HBM, not the 256 MiB cache
     wbytes = sum(s.get("G", 1) * s["N"] * s["K"] for _, s in wl["layers"])
     copies = int(min(64, max(1, math.ceil(args.cache_bytes / wbytes))))
     layers = [build_layer(dg, torch, kind, s, args.seed + i, copies) for i, (kind, s) in enumerate(wl["layers"])]
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    if args.copy_calibration:
+        src = torch.empty(64 * 2 ** 20, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(c):
         for L in layers:
-            run_layer(dg, L, i)
+            run_layer(dg, L, c)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, events around every launch on the current stream
-    ev = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        for L in layers:
-            run_layer(dg, L, args.warmup + i, ev)
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    # one graph per weight copy, each holding one whole step (casts + GEMMs)
+    step_graphs = [capture(torch, lambda c=c: step(c)) for c in range(copies)]
+    time_graphs(torch, step_graphs, min(args.warmup, 2 * copies))
+    total_ms = time_graphs(torch, step_graphs, args.steps)
     ms_per_step = total_ms / args.steps
 
-    per = {}
-    for label, L, e0, e1 in ev:
-        key = (label, id(L))
-        per.setdefault(key, [L, label, 0.0, 0])
-        per[key][2] += e0.elapsed_time(e1)
-        per[key][3] += 1
+    # per-kernel timing: graphs of back-to-back launches of one kernel, same weight copies
+    reps = args.kernel_reps or args.steps
     kernels = []
     step_flops = 0.0
     for L in layers:
-        f, b = layer_work(L["kind"], L["s"], L["valid"])
+        f, _ = layer_work(L["kind"], L["s"], L["valid"])
         step_flops += f
-    for (label, _), (L, lab, ms, n) in per.items():
-        avg_us = ms / n * 1e3
-        s = L["s"]
-        if lab == "gemm":
-            f, b = layer_work(L["kind"], s, L["valid"])
-            bound = "hbm" if f / b < RIDGE else "mfma"
-        else:
-            f, b = 0.0, cast_bytes(L["rows"], s["K"])
-            bound = "hbm"
-        kernels.append({"kernel": lab, "layer": "%s N=%d K=%d" % (L["kind"], s["N"], s["K"]), "avg_us": avg_us,
-                        "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9, "bound": bound,
-                        "flops": f, "bytes": b})
+    for L in layers:
+        s_ = L["s"]
+        N, K = s_["N"], s_["K"]
+
+        def cast_only(L=L):
+            dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"])
+
+        def gemm_only(c, L=L):
+            qb, sb = L["ws"][c % len(L["ws"])]
+            if L["kind"] == "dense":
+                dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"])
+            elif L["kind"] == "contiguous":
+                dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
+            else:
+                G, Mm = s_["G"], s_["M_max"]
+                dg.grouped_gemm_masked(L["qa"].view(G, Mm, K), L["sa"].view(G, Mm, K // 128), qb, sb, L["meta"],
+                                       expected_m=max(1, L["valid"] // G), d=L["d"])
+
+        g_cast = capture(torch, lambda: [cast_only() for _ in range(copies)])
+        g_gemm = capture(torch, lambda: [gemm_only(c) for c in range(copies)])
+        for lab, gr in (("cast", g_cast), ("gemm", g_gemm)):
+            n = max(1, reps // copies)
+            time_graphs(torch, [gr], 2)
+            ms = time_graphs(torch, [gr], n)
+            avg_us = ms / (n * copies) * 1e3
+            if lab == "gemm":
+                f, b = layer_work(L["kind"], s_, L["valid"])
+                bound = "hbm" if f / b < RIDGE else "mfma"
+            else:
+                f, b = 0.0, cast_bytes(L["rows"], K)
+                bound = "hbm"
+            kernels.append({"kernel": lab, "layer": "%s N=%d K=%d" % (L["kind"], N, K), "avg_us": avg_us,
+                            "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
+                            "bound": bound, "flops": f, "bytes": b, "launches": n * copies})
     dom = max(kernels, key=lambda k: k["avg_us"])
     if dom["bound"] == "hbm":
         achieved, peak, unit = dom["gbs"], PEAK_HBM_GBS, "GB/s"
@@ -289,7 +329,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": wl["desc"], "weight_copies": copies,
-                   "step": "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM, per layer"},
+                   "step": "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM (bf16 out), "
+                           "per layer; replayed from HIP graphs"},
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5),
         "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -72,7 +72,7 @@ __device__ __forceinline__ v8i load_frag_global(const uint8_t* p) {
 template <int BN, int NW, int KPW, Layout L>
 __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
   static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
-  static_assert(BN % 16 == 0 && kQ % BN == 0, "tile must sit inside one weight-scale block");
+  static_assert(BN % 16 == 0, "columns come in 16-wide MFMA strips");
   constexpr int TN = BN / 16;
   __shared__ __attribute__((aligned(16))) float red[NW][64 * BN];
   __shared__ __attribute__((aligned(16))) float sa_x[NW][KPW][64];
@@ -92,7 +92,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
   const uint8_t* A = p.a + (int64_t)g * p.M * K;
   const float* SA = p.sfa + (int64_t)g * p.M * nkb;
   const uint8_t* B = p.b + (int64_t)g * p.N * K;
-  const float* SB = p.sfb + ((int64_t)g * (p.N / kQ) + n0 / kQ) * nkb;
+  // each 16-column strip lies inside one 128-column weight-scale block
+  const float* SBg = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
+  const float* SBj[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) SBj[j] = SBg + ((n0 + 16 * j) / kQ) * nkb;
   uint16_t* D = p.d + (int64_t)g * p.M * p.N;
 
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 
   for (int base = w; base < nkb; base += NW * KPW) {
     v8i af[KPW][4], bf[KPW][TN];
-    float sam[KPW], sbv[KPW];
+    float sam[KPW], sbv[KPW][TN];
 #pragma unroll
     for (int u = 0; u < KPW; ++u) {
       const int kb = base + NW * u;
@@ -123,7 +127,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[u][i] = load_frag_global(arow[i] + (int64_t)kc * kQ);
       sam[u] = sarow[kc];
-      sbv[u] = kb < nkb ? SB[kc] : 0.0f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sbv[u][j] = SBj[j][kc] * (kb < nkb ? 1.0f : 0.0f);
     }
     // this lane's output rows of strip i are 16*i + 4*(l>>4) + r: route the activation
     // scales there through the wave's private LDS slots
@@ -134,9 +139,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 s4 = *reinterpret_cast<const float4*>(&sa_x[w][u][16 * i + 4 * (l >> 4)]);
-        const float t0 = s4.x * sbv[u], t1 = s4.y * sbv[u], t2 = s4.z * sbv[u], t3 = s4.w * sbv[u];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+          const float t0 = s4.x * sbv[u][j], t1 = s4.y * sbv[u][j], t2 = s4.z * sbv[u][j], t3 = s4.w * sbv[u][j];
           const v4f pp = mfma_f8_16x16x128(af[u][i], bf[u][j]);
           acc[i][j][0] = fmaf(pp[0], t0, acc[i][j][0]);
           acc[i][j][1] = fmaf(pp[1], t1, acc[i][j][1]);
@@ -522,6 +527,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
 
 template <int BN, int NW, int KPW, Layout L>
 hipError_t run_decode(KParams kp, hipStream_t s) {
+  if (kp.N % BN != 0) return hipErrorInvalidValue;
   kp.tiles_n = (int)(kp.N / BN);
   kp.tiles_m = (int)((kp.M + 63) / 64);
   const int64_t nwg = (int64_t)kp.G * kp.tiles_m * kp.tiles_n;
@@ -874,7 +880,7 @@ bool try_decode_lds(const KParams& kp, hipStream_t s, const char** chosen, hipEr
 #define DG_DECODE_CONFIGS(X) \
   X(16, 8, 2) X(16, 4, 3) X(16, 4, 4) X(16, 6, 2) X(16, 12, 1) X(16, 8, 1) \
   X(32, 4, 3) X(32, 8, 2) X(32, 4, 4) X(32, 6, 2) X(32, 12, 1) X(32, 8, 1) \
-  X(64, 8, 2) X(64, 4, 3) X(64, 4, 4)
+  X(48, 4, 3) X(48, 6, 2) X(48, 8, 2) X(64, 8, 2) X(64, 4, 3) X(64, 4, 4)
 
 template <Layout L>
 hipError_t run_decode_cfg(int bn, int nw, int kpw, const KParams& kp, hipStream_t s, bool* found) {
@@ -900,22 +906,22 @@ hipError_t run_decode_auto(const KParams& kp, hipStream_t s, const char** chosen
   bool forced = false;
   if (env && sscanf(env, "%d,%d,%d", &bn, &nw, &kpw) == 3) forced = true;
   if (!forced) {
-    // One round per wave (all K blocks of a wave in flight at once) and at least ~448
-    // workgroups for the 256 CUs; prefer wider column tiles (less A re-reading).
+    // One round per wave (all K blocks of a wave in flight at once); among those, the
+    // first configuration (measured order) whose workgroup count covers the CUs.
     const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
     const int nkb = kp.nkb;
     struct C { int bn, nw, kpw; };
-    // measured on MI355X (rocprofv3): nkb 12 -> (32,4,3), nkb 16 -> (32,8,2) or (32,12,1)
-    static const C prefs[] = {{32, 4, 3}, {32, 8, 2}, {32, 4, 4}, {16, 8, 2}, {16, 4, 3}, {16, 4, 4}};
+    // measured on MI355X (rocprofv3): nkb 12 -> (48,4,3) or (32,4,3); nkb 16 -> (32,8,2)
+    static const C prefs[] = {{48, 4, 3}, {32, 4, 3}, {32, 8, 2}, {32, 4, 4}, {16, 8, 2}, {16, 4, 3}, {16, 4, 4}};
     bool got = false;
     for (const C& c : prefs) {
-      if (c.nw * c.kpw < nkb) continue;
-      if (rowblocks * (kp.N / c.bn) < 448) continue;
+      if (c.nw * c.kpw < nkb || kp.N % c.bn != 0) continue;
+      if (rowblocks * (kp.N / c.bn) < 200) continue;
       bn = c.bn; nw = c.nw; kpw = c.kpw; got = true;
       break;
     }
     if (!got) {
-      if (rowblocks * (kp.N / 32) >= 448) { bn = 32; nw = 8; kpw = 2; }
+      if (rowblocks * (kp.N / 32) >= 200) { bn = 32; nw = 8; kpw = 2; }
       else { bn = 16; nw = 8; kpw = 2; }
     }
   }
