@@ -100,7 +100,7 @@ def build_layer(dg, torch, kind, s, seed, copies):
         mm = synth.masked_layout(s["G"], s["M_max"], seed)
         rows = s["G"] * s["M_max"]
         valid = int(mm.sum())
-        a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
+        a = torch.randn((s["G"], s["M_max"], K), generator=gen, device=dev, dtype=torch.float32)
         meta = torch.from_numpy(mm).to(dev)
         G = s["G"]
     ws = []
@@ -112,8 +112,9 @@ def build_layer(dg, torch, kind, s, seed, copies):
             ws.append((qb, sb))
         else:
             ws.append((qb.view(G, N, K), sb.view(G, N // 128, K // 128)))
-    qa = torch.empty((rows, K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((rows, K // 128), dtype=torch.float32, device=dev)
+    # activation scales are K-block-major: [K/128, rows], per group for the masked layout
+    qa = torch.empty(tuple(a.shape), dtype=torch.uint8, device=dev)
+    sa = torch.empty(tuple(a.shape[:-2]) + (K // 128, a.shape[-2]), dtype=torch.float32, device=dev)
     if kind == "masked":
         d = torch.empty((s["G"], s["M_max"], N), dtype=torch.bfloat16, device=dev)
     else:
@@ -132,9 +133,8 @@ def run_layer(dg, L, copy_idx):
     elif kind == "contiguous":
         dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
     else:
-        G, Mm = s["G"], s["M_max"]
-        dg.grouped_gemm_masked(L["qa"].view(G, Mm, K), L["sa"].view(G, Mm, K // 128), qb, sb, L["meta"],
-                               expected_m=max(1, L["valid"] // G), d=L["d"])
+        dg.grouped_gemm_masked(L["qa"], L["sa"], qb, sb, L["meta"], expected_m=max(1, L["valid"] // L["G"]),
+                               d=L["d"])
 
 
 def load_traffic(workload, label):
@@ -296,9 +296,8 @@ def main():
             elif L["kind"] == "contiguous":
                 dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
             else:
-                G, Mm = s_["G"], s_["M_max"]
-                dg.grouped_gemm_masked(L["qa"].view(G, Mm, K), L["sa"].view(G, Mm, K // 128), qb, sb, L["meta"],
-                                       expected_m=max(1, L["valid"] // G), d=L["d"])
+                dg.grouped_gemm_masked(L["qa"], L["sa"], qb, sb, L["meta"],
+                                       expected_m=max(1, L["valid"] // L["G"]), d=L["d"])
 
         g_cast = capture(torch, lambda: [cast_only() for _ in range(copies)])
         g_gemm = capture(torch, lambda: [gemm_only(c) for c in range(copies)])

@@ -22,6 +22,11 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is DEVICE memory owned by the caller, contiguous, row-major,
  *     and 16-byte aligned. The library never allocates, frees or keeps a pointer.
+ *   - Activation scales (sfa) are stored K-block-major: [K/128][M], i.e. for each
+ *     128-wide K block the scales of all M rows are contiguous (with a leading [G] for
+ *     the masked layout). The pages leave the layout open; this one lets a GEMM tile
+ *     fetch the scales of its rows for one K block as one contiguous run. Weight scales
+ *     (sfb) are [N/128][K/128].
  *   - FP8 tensors are raw OCP E4M3FN bytes (uint8_t); bf16 tensors are raw uint16_t bits.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls only
  *     enqueue work on it and return without synchronising; inputs must stay alive
@@ -60,17 +65,19 @@ typedef enum { DG_INPUT_F32 = 0, DG_INPUT_BF16 = 1 } dg_input_dtype_t;
 /*
  * Per-token FP8 cast of activations (DeepSeek-V3 repo review, "Innovations" item 4:
  * one scale per 128 elements; "Risks" item 6: bound 448).
- *   x  [M,K]  fp32 or bf16 (x_dtype), finite values.
- *   q  [M,K]  e4m3 bytes (output).
- *   sf [M,K/128] fp32 scales (output).
+ *   x  [G,M,K]  fp32 or bf16 (x_dtype), finite values; G = 1 for a plain [M,K] tensor.
+ *   q  [G,M,K]  e4m3 bytes (output).
+ *   sf [G,K/128,M] fp32 scales (output), K-block-major: sf[g][j][m] is the scale of
+ *      row m, chunk j of group g. G = 1 gives the sfa of the dense and contiguous GEMMs,
+ *      G groups of M_max rows the sfa of the masked GEMM.
  * For each row m and chunk j = columns [128j, 128j+128):
  *   amax = max |x|; s = amax / 448 (correctly rounded fp32 division);
  *   q = e4m3(x / s) with correctly rounded division, round-to-nearest-even, saturation
  *   to +-448, the sign of zero kept; if s == 0 the chunk gets s = 0 and signed zeros.
- * Requires K % 128 == 0.
+ * Requires K % 128 == 0, G >= 0, G*M < 2^31.
  */
-dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t M, int64_t K,
-                                  uint8_t* q, float* sf, void* stream);
+dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t G, int64_t M,
+                                  int64_t K, uint8_t* q, float* sf, void* stream);
 
 /*
  * Per-block FP8 cast of weights: the same rule as above with the amax taken over each
@@ -85,10 +92,10 @@ dg_status_t dg_cast_fp8_per_block(const void* w, dg_input_dtype_t w_dtype, int64
 /*
  * Dense FP8 GEMM with fine-grained scaling (DeepGEMM article, "~300-line JIT core";
  * launch write-up, "Performance": normal GEMM for dense models).
- *   a   [M,K] e4m3,      sfa [M, K/128] fp32 (per-token scales)
+ *   a   [M,K] e4m3,      sfa [K/128, M] fp32 (per-token scales, K-block-major)
  *   b   [N,K] e4m3,      sfb [N/128, K/128] fp32 (block scales)
  *   d   [M,N] bf16 (output):
- *   d[m,n] = bf16_rne( sum_kb  P_kb[m,n] * sfa[m,kb] * sfb[n/128,kb] ),
+ *   d[m,n] = bf16_rne( sum_kb  P_kb[m,n] * sfa[kb,m] * sfb[n/128,kb] ),
  *   P_kb = the FP8 product sum over K block kb, promoted to fp32 once per block.
  * Requires N % 128 == 0, K % 128 == 0.
  */
@@ -98,7 +105,7 @@ dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b,
 /*
  * MoE grouped GEMM, contiguous layout (DeepGEMM article, "~300-line JIT core": groups
  * formed dynamically along M; launch write-up, "Performance": contiguous layout).
- *   a [M_total,K] e4m3, sfa [M_total,K/128]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
+ *   a [M_total,K] e4m3, sfa [K/128,M_total]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
  *   m_indices [M_total] int32 (device): expert id of each row, or -1 for padding;
  *   d [M_total,N] bf16 (output).
  * Each aligned 128-row block belongs to one expert: the expert of the block's first row.
@@ -115,7 +122,7 @@ dg_status_t dg_grouped_gemm_contiguous(const uint8_t* a, const float* sfa, const
 /*
  * MoE grouped GEMM, masked layout (DeepGEMM article, "~300-line JIT core": the masked
  * layout interfaces with the communication library; launch write-up, "Performance").
- *   a [G,M_max,K] e4m3, sfa [G,M_max,K/128]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
+ *   a [G,M_max,K] e4m3, sfa [G,K/128,M_max]; b [G,N,K] e4m3, sfb [G,N/128,K/128];
  *   masked_m [G] int32 (device): valid rows of each group, clamped to [0, M_max];
  *   d [G,M_max,N] bf16 (output).
  * Rows r < masked_m[g] of group g are computed; rows r >= masked_m[g] are not written.

@@ -5,8 +5,12 @@ PyTorch supplies device memory and the current stream; FP8 tensors travel as tor
 (raw OCP E4M3FN bytes) and bf16 outputs as torch.bfloat16. There is no CPU fallback:
 if libdg.so is missing or fails to load, every call raises.
 
+Activation scales are K-block-major ([K/128, M], leading [G] for the masked layout), as
+include/dg.h specifies; weight scales are [N/128, K/128].
+
 Entry points (same names as the C ABI, without the dg_ prefix):
-  cast_fp8_per_token(x)                      -> (q [M,K] uint8, sf [M,K/128] fp32)
+  cast_fp8_per_token(x)                      -> (q [M,K] uint8, sf [K/128,M] fp32)
+                                                (x [G,M,K] -> q [G,M,K], sf [G,K/128,M])
   cast_fp8_per_block(w)                      -> (q [N,K] uint8, sf [N/128,K/128] fp32)
   gemm_fp8_nt(a, sfa, b, sfb)                -> d [M,N] bf16
   grouped_gemm_contiguous(a, sfa, b, sfb, m_indices)      -> d [M_total,N] bf16
@@ -48,7 +52,7 @@ def lib() -> ctypes.CDLL:
                               "or __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        L.dg_cast_fp8_per_token.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
+        L.dg_cast_fp8_per_token.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, P]
         L.dg_cast_fp8_per_block.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
         L.dg_gemm_fp8_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P]
         L.dg_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
@@ -89,15 +93,22 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 # ---- casts ---------------------------------------------------------------------------
 def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None):
-    """x [M,K] fp32/bf16 -> (q [M,K] uint8 e4m3, sf [M,K/128] fp32)."""
+    """x [M,K] or [G,M,K] fp32/bf16 -> (q uint8 e4m3 of x's shape, sf fp32 [K/128,M] or
+    [G,K/128,M]: K-block-major, the sfa layout of the GEMMs)."""
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("x must be float32 or bfloat16")
     _need(x, x.dtype, "x")
-    M, K = x.shape
-    q = torch.empty((M, K), dtype=torch.uint8, device=x.device) if q is None else q
-    sf = torch.empty((M, K // 128), dtype=torch.float32, device=x.device) if sf is None else sf
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be [M,K] or [G,M,K]")
+    G = x.shape[0] if x.dim() == 3 else 1
+    M, K = x.shape[-2:]
+    lead = tuple(x.shape[:-2])
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    sf = torch.empty(lead + (K // 128, M), dtype=torch.float32, device=x.device) if sf is None else sf
+    if tuple(q.shape) != tuple(x.shape) or tuple(sf.shape) != lead + (K // 128, M):
+        raise ValueError("q %s / sf %s do not match x %s" % (tuple(q.shape), tuple(sf.shape), tuple(x.shape)))
     dt = INPUT_BF16 if x.dtype == torch.bfloat16 else INPUT_F32
-    _check(lib().dg_cast_fp8_per_token(_ptr(x), dt, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
+    _check(lib().dg_cast_fp8_per_token(_ptr(x), dt, G, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
     return q, sf
 
 
@@ -127,11 +138,11 @@ def _operands(a, sfa, b, sfb):
 
 
 def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = SCHED_AUTO):
-    """a [M,K] e4m3, sfa [M,K/128], b [N,K] e4m3, sfb [N/128,K/128] -> d [M,N] bf16 = A * B^T."""
+    """a [M,K] e4m3, sfa [K/128,M], b [N,K] e4m3, sfb [N/128,K/128] -> d [M,N] bf16 = A * B^T."""
     _operands(a, sfa, b, sfb)
     M, K = a.shape
     N = b.shape[0]
-    if tuple(b.shape) != (N, K) or tuple(sfa.shape) != (M, K // 128) or tuple(sfb.shape) != (N // 128, K // 128):
+    if tuple(b.shape) != (N, K) or tuple(sfa.shape) != (K // 128, M) or tuple(sfb.shape) != (N // 128, K // 128):
         raise ValueError("shape mismatch: a %s sfa %s b %s sfb %s" % (tuple(a.shape), tuple(sfa.shape),
                                                                     tuple(b.shape), tuple(sfb.shape)))
     d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
@@ -147,13 +158,13 @@ def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = S
 
 def grouped_gemm_contiguous(a, sfa, b, sfb, m_indices, d: torch.Tensor | None = None,
                             schedule: int = SCHED_AUTO):
-    """a [M_total,K], sfa [M_total,K/128], b [G,N,K], sfb [G,N/128,K/128], m_indices [M_total]
+    """a [M_total,K], sfa [K/128,M_total], b [G,N,K], sfb [G,N/128,K/128], m_indices [M_total]
     int32 (expert id or -1) -> d [M_total,N] bf16."""
     _operands(a, sfa, b, sfb)
     _need(m_indices, torch.int32, "m_indices")
     M, K = a.shape
     G, N, _ = b.shape
-    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (M, K // 128)
+    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (K // 128, M)
             or tuple(sfb.shape) != (G, N // 128, K // 128) or tuple(m_indices.shape) != (M,)):
         raise ValueError("shape mismatch")
     d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
@@ -170,13 +181,13 @@ def grouped_gemm_contiguous(a, sfa, b, sfb, m_indices, d: torch.Tensor | None = 
 
 def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.Tensor | None = None,
                         schedule: int = SCHED_AUTO):
-    """a [G,M_max,K], sfa [G,M_max,K/128], b [G,N,K], sfb [G,N/128,K/128], masked_m [G] int32
+    """a [G,M_max,K], sfa [G,K/128,M_max], b [G,N,K], sfb [G,N/128,K/128], masked_m [G] int32
     -> d [G,M_max,N] bf16 (rows >= masked_m[g] are left untouched)."""
     _operands(a, sfa, b, sfb)
     _need(masked_m, torch.int32, "masked_m")
     G, M, K = a.shape
     N = b.shape[1]
-    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (G, M, K // 128)
+    if (tuple(b.shape) != (G, N, K) or tuple(sfa.shape) != (G, K // 128, M)
             or tuple(sfb.shape) != (G, N // 128, K // 128) or tuple(masked_m.shape) != (G,)):
         raise ValueError("shape mismatch")
     d = torch.empty((G, M, N), dtype=torch.bfloat16, device=a.device) if d is None else d

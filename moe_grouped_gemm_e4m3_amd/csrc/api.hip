@@ -96,21 +96,23 @@ dg_status_t run_gemm(dg::Layout layout, int schedule, const uint8_t* a, const fl
   return launched(e, name);
 }
 
-dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int64_t rows, int64_t K,
-                     uint8_t* q, float* sf, void* stream) {
+dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int64_t groups, int64_t rows,
+                     int64_t K, uint8_t* q, float* sf, void* stream) {
   const char* name = per_block ? "dg_cast_fp8_per_block" : "dg_cast_fp8_per_token";
   if (dtype != DG_INPUT_F32 && dtype != DG_INPUT_BF16) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, (int)dtype);
-  if (rows < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
+  if (groups < 0 || rows < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
   if (K % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld is not a multiple of 128", name, (long long)K);
   if (per_block && rows % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: N=%lld is not a multiple of 128", name, (long long)rows);
-  if (rows >= kMaxDim || K >= kMaxDim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: size >= 2^31", name);
-  if (rows == 0 || K == 0) return ok();
+  if (groups >= kMaxDim || rows >= kMaxDim || K >= kMaxDim || (groups > 0 && rows >= kMaxDim / groups))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: size >= 2^31", name);
+  if (groups == 0 || rows == 0 || K == 0) return ok();
   if (!x || !q || !sf) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
   dg_status_t st = check_device();
   if (st != DG_OK) return st;
   hipError_t e = per_block ? dg::launch_cast_per_block(x, dtype == DG_INPUT_BF16, rows, K, q, sf, static_cast<hipStream_t>(stream))
-                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, rows, K, q, sf, static_cast<hipStream_t>(stream));
+                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, groups, rows, K, q, sf,
+                                                       static_cast<hipStream_t>(stream));
   return launched(e, name);
 }
 
@@ -118,14 +120,14 @@ dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int6
 
 extern "C" {
 
-dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t M, int64_t K, uint8_t* q,
-                                  float* sf, void* stream) {
-  return run_cast(false, x, x_dtype, M, K, q, sf, stream);
+dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t G, int64_t M, int64_t K,
+                                  uint8_t* q, float* sf, void* stream) {
+  return run_cast(false, x, x_dtype, G, M, K, q, sf, stream);
 }
 
 dg_status_t dg_cast_fp8_per_block(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K, uint8_t* q,
                                   float* sf, void* stream) {
-  return run_cast(true, w, w_dtype, N, K, q, sf, stream);
+  return run_cast(true, w, w_dtype, 1, N, K, q, sf, stream);
 }
 
 dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,

@@ -37,17 +37,20 @@ __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
 }
 
 // 32 lanes per 128-element chunk, 4 elements per lane; a 256-thread block covers 8
-// chunks per pass and walks the chunks grid-stride. Chunk c of a row-major [M,K]
-// tensor is row c / (K/128), column block c % (K/128), so sf[c] is the [M][K/128] slot.
-template <bool kBf16>
-__global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x,
-                                                             int64_t nchunks,
-                                                             uint8_t* __restrict__ q,
+// chunks per pass and walks the chunks grid-stride. Chunks are numbered in the order of
+// the scale tensor [G][K/128][M] (row fastest): chunk c is row r = c % M, K block
+// kb = (c / M) % (K/128), group g = c / (M * K/128), so sf[c] is its own scale and the 8
+// scales of a pass are 32 contiguous bytes. Idx is uint32_t when the chunk count fits.
+template <bool kBf16, typename Idx>
+__global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x, Idx nchunks,
+                                                             Idx M, Idx kblocks, uint8_t* __restrict__ q,
                                                              float* __restrict__ sf) {
   const int lane = threadIdx.x & 31;
-  for (int64_t c = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); c < nchunks;
-       c += (int64_t)gridDim.x * 8) {
-    const int64_t e0 = c * kQ + lane * 4;
+  const int64_t K = (int64_t)kblocks * kQ;
+  for (Idx c = (Idx)blockIdx.x * 8 + (Idx)(threadIdx.x >> 5); c < nchunks; c += (Idx)gridDim.x * 8) {
+    const Idx gk = c / M, r = c - gk * M;
+    const Idx g = gk / kblocks, kb = gk - g * kblocks;
+    const int64_t e0 = ((int64_t)g * (int64_t)M + (int64_t)r) * K + (int64_t)kb * kQ + lane * 4;
     float v[4];
     load4<kBf16>(x, e0, v);
     float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -95,15 +98,21 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const void* __restr
 
 }  // namespace
 
-hipError_t launch_cast_per_token(const void* x, int bf16, int64_t M, int64_t K, uint8_t* q,
+hipError_t launch_cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q,
                                  float* sf, hipStream_t stream) {
-  const int64_t nchunks = M * (K / kQ);
+  const int64_t kblocks = K / kQ;
+  const int64_t nchunks = G * M * kblocks;
   int64_t blocks = (nchunks + 7) / 8;
   if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 blocks per CU
-  if (bf16)
-    cast_per_token_kernel<true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nchunks, q, sf);
-  else
-    cast_per_token_kernel<false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(x, nchunks, q, sf);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (nchunks < ((int64_t)1 << 32) - 8 * 8192) {  // c + one grid stride stays below 2^32
+    const uint32_t n = (uint32_t)nchunks, m = (uint32_t)M, kbs = (uint32_t)kblocks;
+    if (bf16) cast_per_token_kernel<true, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
+    else cast_per_token_kernel<false, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
+  } else {
+    if (bf16) cast_per_token_kernel<true, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
+    else cast_per_token_kernel<false, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
+  }
   return hipGetLastError();
 }
 

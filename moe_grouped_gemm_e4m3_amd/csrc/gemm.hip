@@ -20,9 +20,11 @@
 //    so neighbouring tiles share an L2.
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "dg_device.h"
 #include "dg_launch.h"
+
 
 namespace dg {
 namespace {
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
   const uint8_t* brow[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) brow[j] = B + (n0 + 16 * j + (l & 15)) * K + kof;
-  const float* sarow = SA + clamp_rows(m0 + l, valid - 1) * nkb;
+  const float* sacol = SA + clamp_rows(m0 + l, valid - 1);  // + kb * M: K-block-major scales
 
   v4f acc[4][TN];
 #pragma unroll
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
       for (int j = 0; j < TN; ++j) bf[u][j] = load_frag_global(brow[j] + (int64_t)kc * kQ);
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[u][i] = load_frag_global(arow[i] + (int64_t)kc * kQ);
-      sam[u] = sarow[kc];
+      sam[u] = sacol[(int64_t)kc * p.M];
 #pragma unroll
       for (int j = 0; j < TN; ++j) sbv[u][j] = SBj[j][kc] * (kb < nkb ? 1.0f : 0.0f);
     }
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_lds_kernel(KParams p) {
     }
     for (int i = t; i < 64 * nkb; i += 64 * NW) {
       const int kb = i >> 6, row = i & 63;
-      sSa[i] = SA[clamp_rows(m0 + row, valid - 1) * nkb + kb];
+      sSa[i] = SA[(int64_t)kb * p.M + clamp_rows(m0 + row, valid - 1)];
     }
   }
 
@@ -438,7 +440,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
     gb[u] = B + (n0 + row) * K + ch * 16;
     lb[u] = row * kQ + ((ch ^ (row & 7)) << 4);
   }
-  const float* gsa = SA + clamp_rows(m0 + (t < BM ? t : 0), valid - 1) * nkb;
+  const float* gsa = SA + clamp_rows(m0 + (t < BM ? t : 0), valid - 1);  // + kb * M
 
   v4i ra[ACH], rb[BCH];
   float rsa = 0.f;
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
     for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga[u] + (int64_t)kb * kQ);
 #pragma unroll
     for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb[u] + (int64_t)kb * kQ);
-    if (t < BM) rsa = gsa[kb];
+    if (t < BM) rsa = gsa[(int64_t)kb * p.M];
   };
   auto lstore = [&](int buf) {
 #pragma unroll
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   // every thread loads and stores an activation scale (threads t and t+BM duplicate one
   // row): no divergent branch inside the pipelined loop
   const int srow = t % BM;
-  const float* gsa = SA + clamp_rows(m0 + srow, valid - 1) * nkb;
+  const float* gsa = SA + clamp_rows(m0 + srow, valid - 1);  // + kb * M
   // byte offsets of the staged A rows from the first one (rows past the valid count are
   // clamped to the last valid row); B rows are always in range
   uint32_t aoff[ACH];
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
     for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga + aoff[u] + ko);
 #pragma unroll
     for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb + bstep * u + ko);
-    const float sa = gsa[kb];
+    const float sa = gsa[(int64_t)kb * p.M];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) rs[nb] = sa * SB[nb * nkb + kb];
   };
@@ -765,6 +767,270 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// tile schedule, direct-to-LDS loads into a three-stage ring
+// ---------------------------------------------------------------------------------
+// Global loads write LDS directly (global_load_lds_dwordx4 / _dword: lane i of a wave
+// writes bytes [16i, 16i+16) (or [4i, 4i+4)) after the LDS base held in M0), so staging
+// needs no registers. Three LDS stages; the loads for K block kb+3 are issued in the
+// middle of K block kb and waited for in the middle of K block kb+2.
+//
+// Per K block (four strips of 16 rows per wave): strip i+1's A fragment is read while
+// strip i's MFMAs run. After strip 2 nothing more is read from the current stage, so the
+// wave waits for the next stage's loads, joins an LDS-only barrier, issues the next loads
+// into the stage just released, and reads the next K block's fragments while strip 3's
+// MFMAs run. MFMA products and promotion factors rotate through two register slots, so
+// every MFMA co-issues with the promotion FMAs of the previous strip.
+//
+// The loads are issued from inline assembly: they write only LDS and have no output
+// registers, and the waits for them are explicit (s_waitcnt vmcnt + an LDS-only barrier).
+// The loop issues no other vector-memory loads (weight scales are staged in LDS up
+// front), so the explicit vmcnt values count exactly these loads. An address is a
+// wave-uniform 64-bit base plus a per-lane 32-bit offset.
+__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kMaxKb3 = 256;  // K blocks the direct-load tile kernel supports (K <= 32768)
+
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
+  constexpr int NW = WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int NB = BN > (int)kQ ? BN / (int)kQ : 1;
+  constexpr int ADMA = BM * 8 / (64 * NW);  // 1 KB direct loads per wave per K block (A)
+  constexpr int BDMA = BN * 8 / (64 * NW);  // (B)
+  constexpr int SROWS = BM / NW;            // activation-scale rows loaded per wave
+  constexpr int PER_STAGE = ADMA + BDMA + 1;
+  constexpr int STAGE_BYTES = (BM + BN) * (int)kQ + BM * 4;
+  static_assert(ADMA * 64 * NW == BM * 8 && BDMA * 64 * NW == BN * 8, "direct-load split");
+  static_assert(SROWS >= 1 && SROWS <= 64 && SROWS * NW == BM, "scale rows per wave");
+  static_assert((BN % kQ == 0 || kQ % BN == 0) && kQ % WTN == 0, "tile vs weight-scale blocks");
+  static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
+  static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
+  static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
+  static_assert(STAGES * STAGE_BYTES + NB * kMaxKb3 * 4 <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float sSB[NB][kMaxKb3];  // this tile's weight scales
+
+  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
+  int g = 0, tm, tn;
+  if constexpr (L == Layout::Masked) {
+    tm = (int)(wg % (uint32_t)p.tiles_m);
+    tn = (int)((wg / (uint32_t)p.tiles_m) % (uint32_t)p.tiles_n);
+    g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  } else {
+    constexpr int GM = 8;
+    const int per_band = GM * p.tiles_n;
+    const int band = (int)wg / per_band;
+    const int first = band * GM;
+    const int gm = min(p.tiles_m - first, GM);
+    const int in = (int)wg % per_band;
+    tm = first + in % gm;
+    tn = in / gm;
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  int64_t valid = p.M;
+  if constexpr (L == Layout::Masked) {
+    valid = clamp_rows(p.masked_m[g], p.M);
+    if (m0 >= valid) return;
+  }
+  if constexpr (L == Layout::Contiguous) {
+    g = p.m_indices[m0];
+    if (g < 0 || g >= p.G) return;
+  }
+  const int nkb = p.nkb;
+  const int64_t K = p.K;
+  const uint8_t* A = p.a + (L == Layout::Masked ? (int64_t)g * p.M * K : 0);
+  const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0);
+  const uint8_t* B = p.b + (int64_t)g * p.N * K;
+  const float* SB = p.sfb + ((int64_t)g * (p.N / kQ) + n0 / kQ) * nkb;
+  uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
+
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform
+  const int wm = w % WM, wn = w / WM;
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+
+  // per-lane 32-bit source offsets of this wave's direct loads; LDS layout of a stage:
+  // A [BM][128] | B [BN][128] | sa [BM] floats, 16-byte chunks XOR-swizzled by (row & 7)
+  uint32_t aoff[ADMA], boff[BDMA];
+#pragma unroll
+  for (int u = 0; u < ADMA; ++u) {
+    const int row = (u * NW + w) * 8 + (l >> 3);
+    aoff[u] = (uint32_t)(clamp_rows(m0 + row, valid - 1) * K) + (uint32_t)(((l & 7) ^ ((l >> 3) & 7)) << 4);
+  }
+#pragma unroll
+  for (int u = 0; u < BDMA; ++u) {
+    const int row = (u * NW + w) * 8 + (l >> 3);
+    boff[u] = (uint32_t)((n0 + row) * K) + (uint32_t)(((l & 7) ^ ((l >> 3) & 7)) << 4);
+  }
+  const uint32_t soff = (uint32_t)(clamp_rows(m0 + w * SROWS + (l < SROWS ? l : 0), valid - 1) * 4);
+
+  auto issue = [&](int kb, int stage) {
+    const uint32_t sbase = smem_base + (uint32_t)(stage * STAGE_BYTES);
+    const uint8_t* ab = A + (int64_t)kb * kQ;
+    const uint8_t* bb = B + (int64_t)kb * kQ;
+#pragma unroll
+    for (int u = 0; u < ADMA; ++u) lds_dma16(aoff[u], ab, sbase + (uint32_t)((u * NW + w) * 1024));
+#pragma unroll
+    for (int u = 0; u < BDMA; ++u) lds_dma16(boff[u], bb, sbase + (uint32_t)(BM * kQ + (u * NW + w) * 1024));
+    if (l < SROWS) lds_dma4(soff, SA + (int64_t)kb * p.M, sbase + (uint32_t)((BM + BN) * kQ + w * SROWS * 4));
+  };
+
+  // the tile's weight scales for every K block, through LDS: the loop below must issue no
+  // vector-memory load besides the direct-to-LDS ones (its vmcnt waits count only those)
+  for (int i = t; i < NB * nkb; i += 64 * NW) sSB[i / nkb][i % nkb] = SB[(i / nkb) * nkb + i % nkb];
+  __syncthreads();
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = l & 15, g4 = l >> 4;
+  const uint32_t sw0 = (uint32_t)((g4 ^ (fr & 7)) << 4), sw1 = (uint32_t)(((g4 + 4) ^ (fr & 7)) << 4);
+  const uint32_t a_lane = (uint32_t)((wm * WTM + fr) * kQ);
+  const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * WTN + fr) * kQ);
+  const uint32_t s_lane = (uint32_t)((BM + BN) * kQ + (wm * WTM + 4 * g4) * 4);
+  const int wnb = (wn * WTN) / (int)kQ;  // this wave's weight-scale column block
+
+  auto read_b = [&](v8i (&bf)[TN], int stage) {
+    const uint8_t* b_s = smem + stage * STAGE_BYTES + b_lane;
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bf[j] = cat8(*reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw0),
+                   *reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw1));
+  };
+  auto read_a = [&](v8i& af, float4& s4, int stage, int i) {
+    const uint8_t* st = smem + stage * STAGE_BYTES;
+    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw0),
+              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw1));
+    s4 = *reinterpret_cast<const float4*>(st + s_lane + 64 * i);
+  };
+
+  v4f pp[2][TN];
+  float4 tt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    tt[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pp[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  auto promote = [&](int slot, int strip) {
+    const float4 tp = tt[slot];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      acc[strip][j][0] = fmaf(pp[slot][j][0], tp.x, acc[strip][j][0]);
+      acc[strip][j][1] = fmaf(pp[slot][j][1], tp.y, acc[strip][j][1]);
+      acc[strip][j][2] = fmaf(pp[slot][j][2], tp.z, acc[strip][j][2]);
+      acc[strip][j][3] = fmaf(pp[slot][j][3], tp.w, acc[strip][j][3]);
+    }
+    // pin the FMAs here: left alone, the compiler sinks every promotion of a K block below
+    // its last MFMA, which keeps all strips' products live and serialises MFMA and VALU work
+#pragma unroll
+    for (int j = 0; j < TN; ++j) asm volatile("" ::"v"(acc[strip][j]));
+  };
+  // MFMAs of one strip into `slot`, interleaved with the promotion of the other slot
+  auto strip = [&](const v8i& af, const v8i (&bf)[TN], int slot, int prev_strip) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pp[slot][j] = mfma_f8_16x16x128(af, bf[j]);
+    promote(slot ^ 1, prev_strip);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  };
+  auto factor = [](const float4& s4, float sb) {
+    return make_float4(s4.x * sb, s4.y * sb, s4.z * sb, s4.w * sb);
+  };
+
+  // K block kb from stage `st` with B fragments `bf` and strip 0's A fragment `a0`; the
+  // next K block's fragments (stage `sn`) replace them, B as the last strip's MFMAs
+  // consume it
+  auto kblock = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, float4& s0) {
+    const float sb = sSB[wnb][kb];
+    v8i af[2];
+    float4 s4[2];
+    af[0] = a0;
+    s4[0] = s0;
+#pragma unroll
+    for (int i = 0; i < TM - 1; ++i) {
+      const int c = i & 1;
+      read_a(af[c ^ 1], s4[c ^ 1], st, i + 1);
+      strip(af[c], bf, c, i == 0 ? TM - 1 : i - 1);  // strip 0 promotes the previous K block's last
+      tt[c] = factor(s4[c], sb);
+    }
+    // every read of stage st is issued; wait for the next stage, then recycle stage st
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    lds_barrier();
+    issue(min(kb + STAGES, nkb - 1), st);  // past the end: a harmless reload
+    read_a(a0, s0, sn, 0);
+    // last strip (odd slot): B fragment j is reloaded from stage sn right after the MFMA
+    // that last reads it
+#pragma unroll
+    for (int j = 0; j < TN; ++j) pp[1][j] = mfma_f8_16x16x128(af[1], bf[j]);
+    promote(0, TM - 2);
+    read_b(bf, sn);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    tt[1] = factor(s4[1], sb);
+  };
+
+  // prologue: the first STAGES K blocks in flight; wait for K block 0
+#pragma unroll
+  for (int q = 0; q < STAGES; ++q) issue(min(q, nkb - 1), q);
+  wait_vmcnt<(STAGES - 1) * PER_STAGE>();
+  lds_barrier();
+  v8i bf[TN], a0;
+  float4 s0;
+  read_b(bf, 0);
+  read_a(a0, s0, 0, 0);
+  int st = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int sn = st == STAGES - 1 ? 0 : st + 1;
+    kblock(kb, st, sn, bf, a0, s0);
+    st = sn;
+  }
+  promote(1, TM - 1);  // the last strip (odd slot)
+  wait_vmcnt<0>();     // drain the tail reloads before leaving
+
+  // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t row = m0 + wm * WTM + 16 * i + 4 * g4 + r;
+      if (row < valid) {
+        uint16_t* drow = D + row * p.N + n0 + wn * WTN + fr;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) drow[16 * j] = (uint16_t)bf16_rne(acc[i][j][r]);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, Layout L>
 hipError_t run_tile2(KParams kp, hipStream_t s) {
   kp.tiles_n = (int)(kp.N / BN);
@@ -774,6 +1040,23 @@ hipError_t run_tile2(KParams kp, hipStream_t s) {
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
   gemm_tile2_kernel<BM, BN, WM, WN, L><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+  return hipGetLastError();
+}
+
+// direct-to-LDS tile schedule; hipErrorNotSupported when the problem exceeds what its
+// 32-bit per-lane offsets or its LDS table of weight scales can address
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L>
+hipError_t run_tile3(KParams kp, hipStream_t s) {
+  if (kp.N % BN != 0 || kp.nkb > kMaxKb3 || kp.M * kp.K >= ((int64_t)1 << 32) ||
+      kp.N * kp.K >= ((int64_t)1 << 32) || kp.M * kp.nkb * 4 >= ((int64_t)1 << 32))
+    return hipErrorNotSupported;
+  kp.tiles_n = (int)(kp.N / BN);
+  kp.tiles_m = (int)((kp.M + BM - 1) / BM);
+  const int64_t nwg = (int64_t)(L == Layout::Masked ? kp.G : 1) * kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -955,50 +1238,86 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   }
   if (p.layout == Layout::Contiguous && sched != Schedule::Tile128) sched = Schedule::Tile128;
 
-  // DG_TILE_V1=1 selects the single-stage tile kernel (for comparison while tuning);
-  // DG_TILE_SHAPE=BMxBN forces one of the instantiated deep-prefetch tiles.
+  // DG_TILE=<name> forces one of the tile kernels below where it applies (for tuning and
+  // for tests that compare them); DG_TILE_V1=1 selects the single-stage tile kernel.
+  const char* force = getenv("DG_TILE");
   const bool v1 = getenv("DG_TILE_V1") != nullptr;
-  int fbm = 0, fbn = 0;
-  if (const char* e = getenv("DG_TILE_SHAPE")) sscanf(e, "%dx%d", &fbm, &fbn);
+  auto is = [&](const char* name) { return force && strcmp(force, name) == 0; };
+  auto pick = [&](const char* name) { if (chosen) *chosen = name; };
   switch (p.layout) {
     case Layout::Dense:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Dense>(kp, stream, chosen);
       if (v1) {
-        if (chosen) *chosen = "tile_v1_128x128";
+        pick("tile_v1_128x128");
         return run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream);
       }
-      if (fbm == 128 && fbn == 256 && kp.N % 256 == 0) {
-        if (chosen) *chosen = "tile_128x256";
-        return run_tile2<128, 256, 2, 4, Layout::Dense>(kp, stream);
-      }
-      if (sched == Schedule::Tile256 || (fbm == 256 && fbn == 128)) {
-        if (chosen) *chosen = "tile_256x128";
+      if (is("t2_256x128")) {
+        pick("tile2_256x128");
         return run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
       }
-      if (chosen) *chosen = "tile_128x128";
+      if (is("t2_128x128")) {
+        pick("tile2_128x128");
+        return run_tile2<128, 128, 2, 4, Layout::Dense>(kp, stream);
+      }
+      if (is("t3_256x128")) {
+        pick("tile3_256x128");
+        const hipError_t e = run_tile3<256, 128, 4, 2, 3, Layout::Dense>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
+      if (is("t3_128x256")) {
+        pick("tile3_128x256");
+        const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Dense>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
+      if (sched == Schedule::Tile256) {
+        pick("tile3_256x256");
+        const hipError_t e = run_tile3<256, 256, 2, 4, 2, Layout::Dense>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+        pick("tile2_256x128");
+        return run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
+      }
+      pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Dense>(kp, stream);
     case Layout::Masked:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Masked>(kp, stream, chosen);
       if (v1) {
-        if (chosen) *chosen = "tile_v1_128x128";
+        pick("tile_v1_128x128");
         return run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream);
       }
       if (sched == Schedule::Tile256) {
-        if (chosen) *chosen = "tile_256x128";
+        if (is("t2_256x128")) {
+          pick("tile2_256x128");
+          return run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
+        }
+        if (is("t3_128x256")) {
+          pick("tile3_128x256");
+          const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Masked>(kp, stream);
+          if (e != hipErrorNotSupported) return e;
+        }
+        pick("tile3_256x256");
+        const hipError_t e = run_tile3<256, 256, 2, 4, 2, Layout::Masked>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+        pick("tile2_256x128");
         return run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
       }
-      if (chosen) *chosen = "tile_128x128";
+      pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Masked>(kp, stream);
     case Layout::Contiguous:
       if (v1) {
-        if (chosen) *chosen = "tile_v1_128x128";
+        pick("tile_v1_128x128");
         return run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
       }
-      if (kp.N % 256 == 0 && !(fbm == 128 && fbn == 128)) {
-        if (chosen) *chosen = "tile_128x256";
+      // the three-stage direct-load ring pays off once K is long enough to fill it
+      if (is("t3_128x256") || (!force && kp.nkb >= 32)) {
+        pick("tile3_128x256");
+        const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Contiguous>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
+      if (kp.N % 256 == 0 && !is("t2_128x128")) {
+        pick("tile2_128x256");
         return run_tile2<128, 256, 2, 4, Layout::Contiguous>(kp, stream);
       }
-      if (chosen) *chosen = "tile_128x128";
+      pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Contiguous>(kp, stream);
   }
   return hipErrorInvalidValue;

@@ -34,10 +34,14 @@ def bf16_values(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_cast_tokens(dg, a_f32: np.ndarray):
-    """Per-token cast on the GPU; returns device (q, sf)."""
-    shp = a_f32.shape
-    q, sf = dg.cast_fp8_per_token(to_dev(a_f32.reshape(-1, shp[-1])))
-    return q.view(*shp), sf.view(*shp[:-1], shp[-1] // 128)
+    """Per-token cast on the GPU of [M,K] or [G,M,K]; returns device (q, sf) with sf in the
+    library's K-block-major layout ([K/128,M] or [G,K/128,M])."""
+    return dg.cast_fp8_per_token(to_dev(a_f32))
+
+
+def kmajor(s: np.ndarray) -> np.ndarray:
+    """Oracle per-token scales [..., M, K/128] in the library's layout [..., K/128, M]."""
+    return np.ascontiguousarray(np.swapaxes(s, -1, -2))
 
 
 def gpu_cast_blocks(dg, w_f32: np.ndarray):
@@ -81,7 +85,7 @@ def quantised_dense(dg, M, N, K, seed=0, outliers=False):
     qa, sa = oracle.cast_per_token(a)
     qb, sb = oracle.cast_per_block(b)
     assert_same_bytes(qa_d, qa, "A cast %dx%d" % (M, K))
-    assert_same_bits(sa_d, sa, "A scales %dx%d" % (M, K))
+    assert_same_bits(sa_d, kmajor(sa), "A scales %dx%d" % (M, K))
     assert_same_bytes(qb_d, qb, "B cast %dx%d" % (N, K))
     assert_same_bits(sb_d, sb, "B scales %dx%d" % (N, K))
     return (qa_d, sa_d, qb_d, sb_d), (qa, sa, qb, sb)

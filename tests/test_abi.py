@@ -92,11 +92,14 @@ def test_grouped_argument_errors(L):
 
 def test_cast_argument_errors(L):
     t = L.dg_cast_fp8_per_token
-    assert t(P, 0, 64, 500, P, P, None) == 2
-    assert t(P, 2, 64, 512, P, P, None) == 1  # unknown dtype
-    assert t(None, 0, 64, 512, P, P, None) == 1
-    assert t(P, 0, 64, 512, Q, P, None) == 3
-    assert t(P, 0, 0, 512, P, P, None) == 0
+    assert t(P, 0, 1, 64, 500, P, P, None) == 2
+    assert t(P, 2, 1, 64, 512, P, P, None) == 1  # unknown dtype
+    assert t(None, 0, 1, 64, 512, P, P, None) == 1
+    assert t(P, 0, 1, 64, 512, Q, P, None) == 3
+    assert t(P, 0, 1, 0, 512, P, P, None) == 0
+    assert t(P, 0, 0, 64, 512, P, P, None) == 0   # G = 0: empty
+    assert t(P, 0, -1, 64, 512, P, P, None) == 1
+    assert t(P, 0, 1 << 20, 1 << 12, 512, P, P, None) == 2  # G*M >= 2^31
     b = L.dg_cast_fp8_per_block
     assert b(P, 0, 100, 512, P, P, None) == 2
     assert b(P, 1, 128, 384, P, Q, None) == 3

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from helpers import (assert_same_bits, assert_same_bytes, gpu_cast_blocks, gpu_cast_tokens, say,
+from helpers import (assert_same_bits, assert_same_bytes, gpu_cast_blocks, gpu_cast_tokens, kmajor, say,
                      to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,8 @@ def test_cast_per_token_bit_exact(dg, M, K, outliers):
     torch.cuda.synchronize()
     qo, so = oracle.cast_per_token(a)
     assert_same_bytes(q, qo, "q")
-    assert_same_bits(s, so, "s")
+    assert tuple(s.shape) == (K // 128, M)
+    assert_same_bits(s, kmajor(so), "s")
 
 
 def test_cast_per_token_edge_chunks(dg):
@@ -52,7 +53,7 @@ def test_cast_per_token_edge_chunks(dg):
     q, s = gpu_cast_tokens(dg, x)
     qo, so = oracle.cast_per_token(x)
     assert_same_bytes(q, qo, "edge q")
-    assert_same_bits(s, so, "edge s")
+    assert_same_bits(s, kmajor(so), "edge s")
     assert so[0, 0] == 0 and so[2, 0] == 0 and so[3, 0] > 0
 
 
@@ -104,7 +105,7 @@ def test_cast_bf16_input(dg):
     q, s = dg.cast_fp8_per_token(xb.to("cuda:0"))
     qo, so = oracle.cast_per_token(xb.float().numpy())
     assert_same_bytes(q, qo, "bf16 q")
-    assert_same_bits(s, so, "bf16 s")
+    assert_same_bits(s, kmajor(so), "bf16 s")
     wb = torch.from_numpy(synth.normal((256, 384), 9, synth.TID_B, 0.02)).to(torch.bfloat16)
     q2, s2 = dg.cast_fp8_per_block(wb.to("cuda:0"))
     qo2, so2 = oracle.cast_per_block(wb.float().numpy())
@@ -121,6 +122,18 @@ def test_cast_per_block_bit_exact(dg, N, K):
     qo, so = oracle.cast_per_block(w)
     assert_same_bytes(q, qo, "block q")
     assert_same_bits(s, so, "block s")
+
+
+@pytest.mark.parametrize("G,M,K", [(3, 40, 384), (4, 128, 512), (2, 1, 128)])
+def test_cast_per_token_grouped(dg, G, M, K):
+    # [G,M,K] activations: scales [G,K/128,M], the masked GEMM's sfa; codes as for [G*M,K]
+    a = synth.normal((G, M, K), 400 + G * M, synth.TID_A)
+    say("cast_per_token grouped %dx%dx%d" % (G, M, K))
+    q, s = gpu_cast_tokens(dg, a)
+    assert tuple(q.shape) == (G, M, K) and tuple(s.shape) == (G, K // 128, M)
+    qo, so = oracle.cast_per_token(a.reshape(G * M, K))
+    assert_same_bytes(q, qo.reshape(G, M, K), "grouped q")
+    assert_same_bits(s, kmajor(so.reshape(G, M, K // 128)), "grouped s")
 
 
 def test_cast_grouped_weights(dg):
@@ -141,4 +154,4 @@ def test_cast_prefill_activation_full_size(dg):
     q, s = gpu_cast_tokens(dg, a)
     qo, so = oracle.cast_per_token(a)
     assert_same_bytes(q, qo, "prefill q")
-    assert_same_bits(s, so, "prefill s")
+    assert_same_bits(s, kmajor(so), "prefill s")

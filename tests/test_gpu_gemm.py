@@ -97,7 +97,7 @@ def test_row_permutation_and_determinism(dg):
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=sched)
         d_again = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=sched)
         assert torch.equal(bf16_bits_t(d), bf16_bits_t(d_again))
-        dp = dg.gemm_fp8_nt(qa[perm].contiguous(), sa[perm].contiguous(), qb, sb, schedule=sched)
+        dp = dg.gemm_fp8_nt(qa[perm].contiguous(), sa[:, perm].contiguous(), qb, sb, schedule=sched)
         assert torch.equal(bf16_bits_t(dp), bf16_bits_t(d[perm]))
 
 
@@ -124,13 +124,13 @@ def test_output_guard_bands(dg):
 def test_zero_and_extreme_scales(dg):
     M, N, K = 64, 256, 512
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=8)
-    sa2 = sa.clone()
-    sa2[:, 1] = 0.0          # a K block switched off
-    sa2[3, :] = 0.0          # a whole row of zero scales
-    sa2[5, :] *= 1e-20       # tiny scales
+    sa2 = sa.clone()         # K-block-major: sa2[kb, m]
+    sa2[1, :] = 0.0          # a K block switched off
+    sa2[:, 3] = 0.0          # a whole row of zero scales
+    sa2[:, 5] *= 1e-20       # tiny scales
     sb2 = sb.clone()
     sb2[1, :] *= 1e15        # large weight scales on the second column block
-    osa2 = sa2.cpu().numpy()
+    osa2 = np.ascontiguousarray(sa2.cpu().numpy().T)
     osb2 = sb2.cpu().numpy()
     R = oracle.gemm(oqa, osa2, oqb, osb2)
     for sched in SCHEDULES.values():
@@ -145,9 +145,35 @@ def test_zero_and_extreme_scales(dg):
 
 def test_empty_problems_launch_nothing(dg):
     a = torch.empty((0, 256), dtype=torch.uint8, device="cuda:0")
-    sa = torch.empty((0, 2), dtype=torch.float32, device="cuda:0")
+    sa = torch.empty((2, 0), dtype=torch.float32, device="cuda:0")
     b = torch.zeros((128, 256), dtype=torch.uint8, device="cuda:0")
     sb = torch.zeros((1, 2), dtype=torch.float32, device="cuda:0")
     say("dense empty M=0")
     d = dg.gemm_fp8_nt(a, sa, b, sb)
     assert tuple(d.shape) == (0, 128)
+
+
+# every tile kernel, forced through DG_TILE (None = the automatic choice); they all sum the
+# K blocks in the same order with the same fp32 operations, so they must agree bit for bit
+TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256"]
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 512, 1280), (512, 256, 2304), (77, 768, 384), (1000, 640, 640),
+                                   (256, 256, 128)])
+def test_tile_kernels_parity_and_agreement(dg, monkeypatch, M, N, K):
+    (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 3)
+    R = oracle.gemm(oqa, osa, oqb, osb)
+    ref = None
+    for v in TILE_VARIANTS:
+        if v:
+            monkeypatch.setenv("DG_TILE", v)
+        else:
+            monkeypatch.delenv("DG_TILE", raising=False)
+        say("dense tile kernel %s M=%d N=%d K=%d" % (v, M, N, K))
+        d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
+        assert_close(bf16_values(d), R, "tile %s" % v)
+        bits = d.view(torch.int16).clone()
+        if ref is None:
+            ref = bits
+        else:
+            assert torch.equal(bits, ref), "tile kernel %s differs from the automatic choice" % v

@@ -39,7 +39,7 @@ def test_cast_and_gemm_graph_replays_match_eager(dg, M, N, K):
     a = torch.from_numpy(a32).to(dev)
     qb, sb = dg.cast_fp8_per_block(torch.from_numpy(b32).to(dev))
     qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device=dev)
     d = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
     def step():
@@ -65,8 +65,7 @@ def test_grouped_graph_replays_match_eager(dg):
     dev = torch.device("cuda:0")
     G, Mm, N, K = 4, 128, 256, 512
     a, b, mm = synth.masked_inputs(G, Mm, N, K, seed=4)
-    qa, sa = dg.cast_fp8_per_token(torch.from_numpy(a.reshape(-1, K)).to(dev))
-    qa, sa = qa.view(G, Mm, K), sa.view(G, Mm, K // 128)
+    qa, sa = dg.cast_fp8_per_token(torch.from_numpy(a).to(dev))
     qb, sb = dg.cast_fp8_per_block(torch.from_numpy(b).to(dev))
     mmd = torch.from_numpy(mm).to(dev)
     d = torch.zeros((G, Mm, N), dtype=torch.bfloat16, device=dev)

@@ -6,7 +6,7 @@ import torch
 import oracle
 import synth
 from helpers import (assert_close, assert_same_bits, assert_same_bytes, bf16_values, gpu_cast_blocks,
-                     gpu_cast_tokens, oracle_cast_tokens, say, to_dev)
+                     gpu_cast_tokens, kmajor, oracle_cast_tokens, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ def _both_sides_contiguous(dg, G, tokens, N, K, seed):
     qa, sa = oracle.cast_per_token(a)
     qb, sb = oracle.cast_per_block(b)
     assert_same_bytes(qa_d, qa, "A")
-    assert_same_bits(sa_d, sa, "sA")
+    assert_same_bits(sa_d, kmajor(sa), "sA")
     assert_same_bytes(qb_d, qb, "B")
     assert_same_bits(sb_d, sb, "sB")
     return (qa_d, sa_d, qb_d, sb_d, to_dev(mi)), (qa, sa, qb, sb, mi)
@@ -43,7 +43,7 @@ def _both_sides_masked(dg, G, M_max, N, K, seed, masked_m=None):
     qa, sa = oracle_cast_tokens(a)
     qb, sb = oracle.cast_per_block(b)
     assert_same_bytes(qa_d, qa, "A")
-    assert_same_bits(sa_d, sa, "sA")
+    assert_same_bits(sa_d, kmajor(sa), "sA")
     assert_same_bytes(qb_d, qb, "B")
     assert_same_bits(sb_d, sb, "sB")
     return (qa_d, sa_d, qb_d, sb_d, to_dev(mm)), (qa, sa, qb, sb, mm)
@@ -61,6 +61,27 @@ def test_contiguous_parity(dg, G, tokens, N, K):
     assert_close(bf16_values(d), R, "contiguous", mask=omi[:, None].repeat(N, 1) >= 0)
 
 
+@pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None])
+def test_contiguous_tile_kernels(dg, monkeypatch, variant):
+    # long enough K for the automatic choice to take the direct-load ring; each kernel checked
+    # against the oracle and against the others bit for bit
+    G, N, K = 3, 512, 4352
+    (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 300, N, K, seed=21)
+    if variant:
+        monkeypatch.setenv("DG_TILE", variant)
+    else:
+        monkeypatch.delenv("DG_TILE", raising=False)
+    say("contiguous tile kernel %s" % variant)
+    d = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
+    R = oracle.grouped_contiguous(oqa, osa, oqb, osb, omi)
+    valid = omi[:, None].repeat(N, 1) >= 0
+    assert_close(bf16_values(d), R, "contiguous %s" % variant, mask=valid)
+    monkeypatch.setenv("DG_TILE", "t2_128x256")
+    d2 = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
+    rows = torch.from_numpy(np.nonzero(omi >= 0)[0]).to("cuda:0")
+    assert torch.equal(d[rows].view(torch.int16), d2[rows].view(torch.int16))
+
+
 def test_contiguous_equals_dense_per_expert_on_gpu(dg):
     G, N, K = 4, 256, 512
     (qa, sa, qb, sb, mi), (_, _, _, _, omi) = _both_sides_contiguous(dg, G, 700, N, K, seed=3)
@@ -68,7 +89,7 @@ def test_contiguous_equals_dense_per_expert_on_gpu(dg):
     d = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
     for g in range(G):
         rows = torch.from_numpy(np.nonzero(omi == g)[0]).to("cuda:0")
-        dd = dg.gemm_fp8_nt(qa[rows].contiguous(), sa[rows].contiguous(), qb[g], sb[g], schedule=2)
+        dd = dg.gemm_fp8_nt(qa[rows].contiguous(), sa[:, rows].contiguous(), qb[g], sb[g], schedule=2)
         assert torch.equal(d[rows].view(torch.int16), dd.view(torch.int16))
 
 
@@ -77,8 +98,8 @@ def test_contiguous_padding_block_untouched(dg):
     G, N, K = 2, 256, 256
     (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 200, N, K, seed=4)
     omi2 = np.concatenate([omi, np.full(128, -1, np.int32)])
-    pad = lambda t, n: torch.cat([t, torch.zeros((128,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)])
-    qa2, sa2 = pad(qa, 128), pad(sa, 128)
+    qa2 = torch.cat([qa, torch.zeros((128, K), dtype=qa.dtype, device=qa.device)])
+    sa2 = torch.cat([sa, torch.zeros((K // 128, 128), dtype=sa.dtype, device=sa.device)], dim=1).contiguous()
     d = torch.full((omi2.size, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("contiguous padding block untouched")
     dg.grouped_gemm_contiguous(qa2, sa2, qb, sb, to_dev(omi2), d=d)
@@ -128,6 +149,26 @@ def test_masked_parity_and_sentinels(dg, sched):
     assert_close(bf16_values(d), R, "masked %s" % sched, mask=valid)
     bits = d.view(torch.int16).cpu().numpy()
     assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
+
+
+@pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128"])
+def test_masked_tile_kernels(dg, monkeypatch, variant):
+    G, M_max, N, K = 5, 300, 512, 768
+    mm = [0, 17, 128, 257, 300]
+    (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 22, mm)
+    monkeypatch.setenv("DG_TILE", variant)
+    d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    say("masked tile kernel %s" % variant)
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["tile256"])
+    R = oracle.grouped_masked(oqa, osa, oqb, osb, omm)
+    valid = np.isfinite(R)
+    assert_close(bf16_values(d), R, "masked %s" % variant, mask=valid)
+    bits = d.view(torch.int16).cpu().numpy()
+    assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
+    monkeypatch.delenv("DG_TILE")
+    d2 = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d2, schedule=MASKED_SCHEDULES["tile256"])
+    assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
 
 
 def test_masked_clamps_out_of_range_counts(dg):
