@@ -54,6 +54,27 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Direct global->LDS loads (global_load_lds_dwordx4 / _dword: lane i of a wave writes
+// bytes [16i, 16i+16) (or [4i, 4i+4)) after the LDS base held in M0). They are issued from
+// inline assembly: they write only LDS and have no output registers; an address is a
+// wave-uniform 64-bit base plus a per-lane 32-bit offset. Waits for them are explicit.
+__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // K split of one 128-byte operand row over the four lane groups g = l >> 4 of an MFMA:
 // group g holds bytes [16g, 16g+16) and [64+16g, 64+16g+16). A and B use the same split,
 // so the products pair up; each 16-byte load instruction of a wave then covers whole
@@ -181,6 +202,168 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
     }
   }
 }
+
+// ---------------------------------------------------------------------------------
+// decode schedule, activation block in LDS
+// ---------------------------------------------------------------------------------
+// Workgroup: 64 rows x BN columns over all of K, NW waves = KG K-groups x (NW/KG) column
+// groups. Every weight byte is read once; the 64 x K activation block is read once per
+// workgroup, straight into LDS with full-line direct loads, instead of once per wave.
+//   1. Each wave issues all its B fragment loads (K blocks kg, kg+KG, ... of its TN strips)
+//      and weight scales, then its share of the activation block and its scales (direct
+//      loads into LDS), then waits for everything and joins a barrier.
+//   2. Per K block: A fragments from LDS (16-byte chunks XOR-swizzled by row), 4 x TN
+//      MFMAs, promotion by sa * sb.
+//   3. The K-groups' partial tiles are summed in a fixed order through LDS (the bytes that
+//      held A) and written as bf16.
+// LDS: A [nkb][64 rows][128 B] | sa [nkb][64] fp32; afterwards the partial tiles.
+template <int BN, int KG, int KPW, int NW, Layout L>
+__global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
+  static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
+  constexpr int SG = NW / KG, TN = BN / 16 / SG;
+  static_assert(SG * KG == NW && TN * 16 * SG == BN, "waves split evenly over K and columns");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
+  const int nt = (int)(wg % (uint32_t)p.tiles_n);
+  const int mb = (int)((wg / (uint32_t)p.tiles_n) % (uint32_t)p.tiles_m);
+  const int g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  const int64_t m0 = (int64_t)mb * 64;
+  int64_t valid = p.M;
+  if constexpr (L == Layout::Masked) valid = clamp_rows(p.masked_m[g], p.M);
+  if (m0 >= valid) return;  // uniform over the workgroup
+  const int64_t n0 = (int64_t)nt * BN;
+  const int nkb = p.nkb;
+  const int64_t K = p.K;
+  const uint8_t* A = p.a + ((L == Layout::Masked ? (int64_t)g * p.M : 0) + m0) * K;  // this row block
+  const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0) + m0;   // + kb * M
+  const uint8_t* B = p.b + (int64_t)g * p.N * K;
+  const float* SBg = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
+  uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
+
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kg = w % KG, sg = w / KG;
+  const int fr = l & 15, g4 = l >> 4;
+  const int rows = (int)(valid - m0 < 64 ? valid - m0 : 64);  // rows >= this are clamped
+
+  // 1. B fragments and weight scales of this wave's K blocks (a K block past the end
+  //    reloads the last one with weight 0)
+  v8i bf[KPW][TN];
+  float sbv[KPW][TN];
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int kb = kg + KG * u;
+    const int kc = kb < nkb ? kb : nkb - 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + 16 * (sg * TN + j);
+      bf[u][j] = load_frag_global(B + (col + fr) * K + (int64_t)kc * kQ + g4 * 16);
+      sbv[u][j] = SBg[(col / kQ) * nkb + kc] * (kb < nkb ? 1.0f : 0.0f);
+    }
+  }
+  //    the activation block: instruction q covers rows 8*(q%8) .. +8 of K block q/8; lane l
+  //    fetches chunk (l&7) ^ (row&7) of its row so that LDS holds the swizzled layout
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  {
+    const int row = (l >> 3);  // + 8 * (q % 8)
+    for (int q = w; q < 8 * nkb; q += NW) {
+      const int kb = q >> 3, rb = q & 7;
+      const int r = 8 * rb + row;
+      const int rc = r < rows ? r : rows - 1;
+      const uint32_t voff = (uint32_t)((int64_t)rc * K) + (uint32_t)(kb * kQ) + (uint32_t)((((l & 7) ^ (r & 7))) << 4);
+      lds_dma16(voff, A, sbase + (uint32_t)(kb * 8192 + rb * 1024));
+    }
+    const uint32_t soff = (uint32_t)((l < rows ? l : rows - 1) * 4);
+    for (int kb = w; kb < nkb; kb += NW)
+      lds_dma4(soff, SA + (int64_t)kb * p.M, sbase + (uint32_t)(nkb * 8192 + kb * 256));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // 2. MFMAs per K block, promotion by sa * sb
+  v4f acc[4][TN];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const uint32_t sw0 = (uint32_t)((g4 ^ (fr & 7)) << 4), sw1 = (uint32_t)(((g4 + 4) ^ (fr & 7)) << 4);
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int kb = kg + KG * u;
+    const int kc = kb < nkb ? kb : nkb - 1;  // weight 0 past the end
+    const uint8_t* ak = smem + kc * 8192 + fr * 128;
+    const float* sk = reinterpret_cast<const float*>(smem + nkb * 8192 + kc * 256) + 4 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v8i af = cat8(*reinterpret_cast<const v4i*>(ak + i * 2048 + sw0),
+                          *reinterpret_cast<const v4i*>(ak + i * 2048 + sw1));
+      const float4 s4 = *reinterpret_cast<const float4*>(sk + 16 * i);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v4f pp = mfma_f8_16x16x128(af, bf[u][j]);
+        acc[i][j][0] = fmaf(pp[0], s4.x * sbv[u][j], acc[i][j][0]);
+        acc[i][j][1] = fmaf(pp[1], s4.y * sbv[u][j], acc[i][j][1]);
+        acc[i][j][2] = fmaf(pp[2], s4.z * sbv[u][j], acc[i][j][2]);
+        acc[i][j][3] = fmaf(pp[3], s4.w * sbv[u][j], acc[i][j][3]);
+      }
+    }
+  }
+
+  // 3. K-group partials: groups 1.. store their fragments (lane-native order), group 0
+  //    adds them in order kg = 1, 2, ... and stores the sum row-major for the bf16 pass
+  __syncthreads();  // every wave is done with A in LDS
+  float4* part = reinterpret_cast<float4*>(smem);
+  constexpr int FR = 4 * TN * 64;  // float4 per partial tile of one wave
+  if (kg > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        part[((kg - 1) * SG + sg) * FR + (i * TN + j) * 64 + l] =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  __syncthreads();
+  float* tile = reinterpret_cast<float*>(part + (KG - 1) * SG * FR);  // [64][BN]
+  if (kg == 0) {
+    for (int k2 = 1; k2 < KG; ++k2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const float4 v = part[((k2 - 1) * SG + sg) * FR + (i * TN + j) * 64 + l];
+          acc[i][j][0] += v.x; acc[i][j][1] += v.y; acc[i][j][2] += v.z; acc[i][j][3] += v.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tile[(16 * i + 4 * g4 + r) * BN + 16 * (sg * TN + j) + fr] = acc[i][j][r];
+  }
+  __syncthreads();
+  constexpr int kGroups = 64 * BN / 4;  // 4 consecutive columns per thread-step
+  for (int e = t; e < kGroups; e += 64 * NW) {
+    const int row = e / (BN / 4);
+    const int c4 = (e % (BN / 4)) * 4;
+    if (row < rows) {
+      const float4 v = *reinterpret_cast<const float4*>(&tile[row * BN + c4]);
+      uint2 o;
+      o.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
+      o.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
+      *reinterpret_cast<uint2*>(D + (m0 + row) * p.N + n0 + c4) = o;
+    }
+  }
+}
+
+inline size_t decode2_need(int bn, int kg, int nkb) {  // bytes of dynamic LDS
+  const size_t a = (size_t)nkb * 8192 + (size_t)nkb * 256;             // A block + its scales
+  const size_t r = (size_t)(kg - 1) * 64 * bn * 4 + (size_t)64 * bn * 4;  // partial tiles + sum
+  return a > r ? a : r;
+}
+
+
 
 // ---------------------------------------------------------------------------------
 // decode schedule with the activation block resident in LDS
@@ -768,42 +951,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------------
-// tile schedule, direct-to-LDS loads into a three-stage ring
+// tile schedule, direct-to-LDS loads into a ring of LDS stages
 // ---------------------------------------------------------------------------------
-// Global loads write LDS directly (global_load_lds_dwordx4 / _dword: lane i of a wave
-// writes bytes [16i, 16i+16) (or [4i, 4i+4)) after the LDS base held in M0), so staging
-// needs no registers. Three LDS stages; the loads for K block kb+3 are issued in the
-// middle of K block kb and waited for in the middle of K block kb+2.
+// A, B and the activation scales of a K block go straight from global memory into one of
+// STAGES LDS stages (no staging registers). The loads for K block kb+STAGES are issued in
+// the middle of K block kb, into the stage kb just released.
 //
-// Per K block (four strips of 16 rows per wave): strip i+1's A fragment is read while
-// strip i's MFMAs run. After strip 2 nothing more is read from the current stage, so the
-// wave waits for the next stage's loads, joins an LDS-only barrier, issues the next loads
-// into the stage just released, and reads the next K block's fragments while strip 3's
+// Per K block a wave runs TM strips of 16 rows: strip i+1's A fragment is read while strip
+// i's MFMAs run. After strip TM-2 nothing more is read from the current stage, so the wave
+// waits for the next stage's loads, joins an LDS-only barrier, issues the loads that refill
+// the stage just released, and reads the next K block's fragments while the last strip's
 // MFMAs run. MFMA products and promotion factors rotate through two register slots, so
 // every MFMA co-issues with the promotion FMAs of the previous strip.
 //
-// The loads are issued from inline assembly: they write only LDS and have no output
-// registers, and the waits for them are explicit (s_waitcnt vmcnt + an LDS-only barrier).
-// The loop issues no other vector-memory loads (weight scales are staged in LDS up
-// front), so the explicit vmcnt values count exactly these loads. An address is a
-// wave-uniform 64-bit base plus a per-lane 32-bit offset.
-__device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
-               "s"(sbase)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff),
-               "s"(sbase)
-               : "memory", "m0");
-}
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
+// The loop issues no vector-memory loads besides the direct ones (the tile's weight scales
+// are staged in LDS up front), so the explicit vmcnt values count exactly those.
 constexpr int kMaxKb3 = 256;  // K blocks the direct-load tile kernel supports (K <= 32768)
 
 template <int BM, int BN, int WM, int WN, int STAGES, Layout L>
@@ -1176,9 +1338,82 @@ hipError_t run_decode_cfg(int bn, int nw, int kpw, const KParams& kp, hipStream_
   return hipSuccess;
 }
 
+template <int BN, int KG, int KPW, int NW, Layout L>
+hipError_t run_decode2(KParams kp, hipStream_t s) {
+  const size_t lds = decode2_need(BN, KG, kp.nkb);
+  if (kp.N % BN != 0 || (int64_t)KG * KPW < kp.nkb || lds > kLdsBytes || 64 * kp.K >= ((int64_t)1 << 32))
+    return hipErrorNotSupported;
+  kp.tiles_n = (int)(kp.N / BN);
+  kp.tiles_m = (int)((kp.M + 63) / 64);
+  const int64_t nwg = (int64_t)kp.G * kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode2_kernel<BN, KG, KPW, NW, L>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  gemm_decode2_kernel<BN, KG, KPW, NW, L><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
+  return hipGetLastError();
+}
+
+// Instantiated configurations of the LDS decode schedule, in order of preference:
+// (columns per workgroup, K-groups, K blocks per wave, waves). Wider workgroups read the
+// activation block fewer times; the first one that covers K, divides N, fits LDS and
+// leaves enough workgroups to cover the CUs is taken.
+#define DG_DECODE2_CONFIGS(X) \
+  X(128, 4, 3, 8) X(96, 4, 3, 8) X(96, 1, 12, 6) X(96, 2, 6, 6) X(64, 8, 2, 8) X(64, 8, 3, 8) X(32, 8, 2, 8) \
+  X(32, 8, 3, 8) X(32, 2, 8, 4) X(32, 4, 4, 4) X(32, 1, 16, 2) X(16, 8, 2, 8) X(16, 8, 3, 8)
+
+template <Layout L>
+hipError_t run_decode2_cfg(int bn, int kg, int kpw, int nw, const KParams& kp, hipStream_t s) {
+#define DG_X(a, b, c, d) \
+  if (bn == a && kg == b && kpw == c && nw == d) return run_decode2<a, b, c, d, L>(kp, s);
+  DG_DECODE2_CONFIGS(DG_X)
+#undef DG_X
+  return hipErrorNotSupported;
+}
+
+// LDS decode schedule if some configuration applies; false leaves the choice to the caller.
+template <Layout L>
+bool try_decode2(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
+  static thread_local char name[48];
+  struct C { int bn, kg, kpw, nw; };
+  static const C cfgs[] = {
+#define DG_X(a, b, c, d) {a, b, c, d},
+      DG_DECODE2_CONFIGS(DG_X)
+#undef DG_X
+  };
+  const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
+  C c{0, 0, 0, 0};
+  const char* env = getenv("DG_DECODE2");  // tuning: "bn,kg,kpw,nw"
+  if (env && sscanf(env, "%d,%d,%d,%d", &c.bn, &c.kg, &c.kpw, &c.nw) == 4) {
+  } else {
+    int64_t best = 0;
+    for (const C& q : cfgs) {
+      if ((int64_t)q.kg * q.kpw < kp.nkb || kp.N % q.bn != 0) continue;
+      if (decode2_need(q.bn, q.kg, kp.nkb) > kLdsBytes) continue;
+      const int64_t wgs = rowblocks * (kp.N / q.bn);
+      if (wgs >= 200) { c = q; best = -1; break; }
+      if (wgs > best) { best = wgs; c = q; }  // otherwise the most workgroups
+    }
+    if (c.bn == 0) return false;
+  }
+  const hipError_t e = run_decode2_cfg<L>(c.bn, c.kg, c.kpw, c.nw, kp, s);
+  if (e == hipErrorNotSupported) return false;
+  *err = e;
+  snprintf(name, sizeof name, "decode2_bn%d_kg%d_kpw%d_w%d", c.bn, c.kg, c.kpw, c.nw);
+  if (chosen) *chosen = name;
+  return true;
+}
+
 template <Layout L>
 hipError_t run_decode_auto(const KParams& kp, hipStream_t s, const char** chosen) {
   static thread_local char name[64];
+  const char* which = getenv("DG_DECODE");  // tuning: "v1" keeps the register-fed schedule
+  if (!(which && strcmp(which, "v1") == 0)) {
+    hipError_t e = hipSuccess;
+    if (try_decode2<L>(kp, s, chosen, &e)) return e;
+  }
   if (getenv("DG_DECODE_LDS")) {  // tuning: the LDS-resident variant
     hipError_t e = hipSuccess;
     if (try_decode_lds<L>(kp, s, chosen, &e)) return e;

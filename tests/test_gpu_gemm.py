@@ -177,3 +177,23 @@ def test_tile_kernels_parity_and_agreement(dg, monkeypatch, M, N, K):
             ref = bits
         else:
             assert torch.equal(bits, ref), "tile kernel %s differs from the automatic choice" % v
+
+
+# decode schedules, forced one by one: the register-fed one (DG_DECODE=v1) and the LDS ones
+# (DG_DECODE2="bn,kg,kpw,waves"); each against the oracle, on full and partial 64-row blocks
+DECODE_VARIANTS = [("DG_DECODE", "v1"), ("DG_DECODE2", "96,4,3,8"), ("DG_DECODE2", "96,1,12,6"),
+                   ("DG_DECODE2", "96,2,6,6"), ("DG_DECODE2", "32,8,2,8"), ("DG_DECODE2", "32,2,8,4"),
+                   ("DG_DECODE2", "32,1,16,2"), ("DG_DECODE2", "16,8,3,8"), ("DG_DECODE2", "128,4,3,8")]
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 1536, 1536), (37, 768, 2048), (1, 384, 1152), (130, 768, 1024)])
+def test_decode_variants(dg, monkeypatch, M, N, K):
+    (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 11)
+    R = oracle.gemm(oqa, osa, oqb, osb)
+    for var, val in DECODE_VARIANTS:
+        monkeypatch.delenv("DG_DECODE", raising=False)
+        monkeypatch.delenv("DG_DECODE2", raising=False)
+        monkeypatch.setenv(var, val)
+        say("decode %s=%s M=%d N=%d K=%d" % (var, val, M, N, K))
+        d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["decode"])
+        assert_close(bf16_values(d), R, "decode %s" % val)
