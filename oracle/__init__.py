@@ -63,6 +63,8 @@ def _L():
         lib.dgo_encode_array.argtypes = [P, I64, P]
         lib.dgo_cast_per_token.argtypes = [P, I64, I64, P, P]
         lib.dgo_cast_per_block.argtypes = [P, I64, I64, P, P]
+        lib.dgo_cast_per_token_pow2.argtypes = [P, I64, I64, P, P]
+        lib.dgo_cast_per_block_pow2.argtypes = [P, I64, I64, P, P]
         lib.dgo_bf16_to_f32.argtypes = [P, I64, P]
         lib.dgo_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
         lib.dgo_gemm_pairs.argtypes = [P, P, P, P, P, I64, I64, P, P, I64, P]
@@ -127,28 +129,31 @@ def bf16_bits_to_f32(x_bits: np.ndarray) -> np.ndarray:
     return out
 
 
-def cast_per_token(x: np.ndarray):
-    """x [M,K] fp32 -> (q [M,K] uint8 e4m3, s [M,K/128] fp32); s = amax/448, q = e4m3(x/s)."""
+def cast_per_token(x: np.ndarray, pow2: bool = False):
+    """x [M,K] fp32 -> (q [M,K] uint8 e4m3, s [M,K/128] fp32); s = amax/448 (pow2: the
+    smallest power of two >= that, at least 2^-126), q = e4m3(x/s)."""
     x = _c(x, np.float32)
     M, K = x.shape
     assert K % QBLK == 0
     q = np.empty((M, K), np.uint8)
     s = np.empty((M, K // QBLK), np.float32)
-    _L().dgo_cast_per_token(_p(x), M, K, _p(q), _p(s))
+    fn = _L().dgo_cast_per_token_pow2 if pow2 else _L().dgo_cast_per_token
+    fn(_p(x), M, K, _p(q), _p(s))
     return q, s
 
 
-def cast_per_block(w: np.ndarray):
+def cast_per_block(w: np.ndarray, pow2: bool = False):
     """w [N,K] (or [G,N,K]) fp32 -> (q uint8 e4m3, s [N/128,K/128] fp32) per 128x128 block."""
     w = _c(w, np.float32)
     if w.ndim == 3:
-        qs = [cast_per_block(w[g]) for g in range(w.shape[0])]
+        qs = [cast_per_block(w[g], pow2) for g in range(w.shape[0])]
         return np.stack([q for q, _ in qs]), np.stack([s for _, s in qs])
     N, K = w.shape
     assert N % QBLK == 0 and K % QBLK == 0
     q = np.empty((N, K), np.uint8)
     s = np.empty((N // QBLK, K // QBLK), np.float32)
-    _L().dgo_cast_per_block(_p(w), N, K, _p(q), _p(s))
+    fn = _L().dgo_cast_per_block_pow2 if pow2 else _L().dgo_cast_per_block
+    fn(_p(w), N, K, _p(q), _p(s))
     return q, s
 
 

@@ -28,7 +28,12 @@
  *  - division x / s is a correctly rounded fp32 division, not a reciprocal multiply;
  *  - an all-zero chunk (or one whose s underflows to 0) stores s = 0 and signed zeros;
  *  - the sign of zero is kept;
- *  - the promotion interval is one 128-wide K block (the scale changes every 128 K).
+ *  - the promotion interval is one 128-wide K block (the scale changes every 128 K);
+ *  - power-of-two (UE8M0) scales, the variant the DeepSeek-V3 repo review names under
+ *    "Innovations" item 4 (scales rounded to powers of two so that scaling is a shift):
+ *    s = the smallest power of two not below fp32(amax / 448), and at least 2^-126 (the
+ *    smallest normal fp32, so that s is never 0); q = e4m3(x / s), where the division is
+ *    exact.
  *
  * The GEMM result R = sum_kb (s_a * s_b) * P_kb is kept in fp64. Each block sum P_kb is
  * exact in fp64: every e4m3 value is a multiple of 2^-9, so each product is a multiple
@@ -150,15 +155,27 @@ void dgo_encode_array(const float* y, int64_t n, uint8_t* out) {
 /* ------------------------------------------------------------------------- */
 /* Casts                                                                      */
 /* ------------------------------------------------------------------------- */
+/* The power-of-two scale of a group: the smallest power of two >= v = fp32(amax/448),
+ * and >= 2^-126. Written with frexp: v = f * 2^e with f in [0.5, 1), so v is a power of
+ * two exactly when f == 0.5. */
+static float pow2_scale(float v) {
+  if (!(v > 0x1p-126f)) return 0x1p-126f;
+  int e;
+  float f = frexpf(v, &e);
+  return f == 0.5f ? v : ldexpf(1.0f, e);
+}
+
 /* Quantise one group of values (a 1x128 chunk or a 128x128 block) that share a
- * scale. `idx` lists the positions of the group's elements. */
-static float quant_group(const float* x, const int64_t* idx, int count, uint8_t* q) {
+ * scale. `idx` lists the positions of the group's elements; pow2 selects power-of-two
+ * scales. */
+static float quant_group(const float* x, const int64_t* idx, int count, uint8_t* q, int pow2) {
   float amax = 0.0f;
   for (int i = 0; i < count; ++i) {
     float v = fabsf(x[idx[i]]);
     if (v > amax) amax = v;
   }
   float s = amax / 448.0f; /* correctly rounded fp32 division */
+  if (pow2) s = pow2_scale(s);
   for (int i = 0; i < count; ++i) {
     float v = x[idx[i]];
     if (s == 0.0f) {
@@ -172,20 +189,26 @@ static float quant_group(const float* x, const int64_t* idx, int count, uint8_t*
 }
 
 /* Per-token cast: x [M,K] fp32 row-major -> q [M,K] e4m3, s [M,K/128] fp32. */
-void dgo_cast_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s) {
+static void cast_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s, int pow2) {
   int64_t nkb = K / QBLK;
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; ++m) {
     int64_t idx[QBLK];
     for (int64_t j = 0; j < nkb; ++j) {
       for (int i = 0; i < QBLK; ++i) idx[i] = m * K + j * QBLK + i;
-      s[m * nkb + j] = quant_group(x, idx, QBLK, q);
+      s[m * nkb + j] = quant_group(x, idx, QBLK, q, pow2);
     }
   }
 }
+void dgo_cast_per_token(const float* x, int64_t M, int64_t K, uint8_t* q, float* s) {
+  cast_per_token(x, M, K, q, s, 0);
+}
+void dgo_cast_per_token_pow2(const float* x, int64_t M, int64_t K, uint8_t* q, float* s) {
+  cast_per_token(x, M, K, q, s, 1);
+}
 
 /* Weight block cast: w [N,K] fp32 -> q [N,K] e4m3, s [N/128, K/128] fp32. */
-void dgo_cast_per_block(const float* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+static void cast_per_block(const float* w, int64_t N, int64_t K, uint8_t* q, float* s, int pow2) {
   int64_t nnb = N / QBLK, nkb = K / QBLK;
 #pragma omp parallel for collapse(2) schedule(static)
   for (int64_t bn = 0; bn < nnb; ++bn) {
@@ -194,9 +217,15 @@ void dgo_cast_per_block(const float* w, int64_t N, int64_t K, uint8_t* q, float*
       int c = 0;
       for (int64_t r = 0; r < QBLK; ++r)
         for (int64_t k = 0; k < QBLK; ++k) idx[c++] = (bn * QBLK + r) * K + bk * QBLK + k;
-      s[bn * nkb + bk] = quant_group(w, idx, QBLK * QBLK, q);
+      s[bn * nkb + bk] = quant_group(w, idx, QBLK * QBLK, q, pow2);
     }
   }
+}
+void dgo_cast_per_block(const float* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+  cast_per_block(w, N, K, q, s, 0);
+}
+void dgo_cast_per_block_pow2(const float* w, int64_t N, int64_t K, uint8_t* q, float* s) {
+  cast_per_block(w, N, K, q, s, 1);
 }
 
 /* bf16 bit patterns -> fp32 (exact widening). */

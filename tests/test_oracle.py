@@ -181,6 +181,62 @@ def test_cast_invariants():
     assert np.array_equal(qp.reshape(64, 16, 128), qc[:, :, perm]) and np.array_equal(sp, s)
 
 
+def _pow2_ceil_reference(amax: np.ndarray) -> np.ndarray:
+    """The reading of power-of-two scales, computed with numpy alone: the smallest power of
+    two >= fp32(amax/448), at least 2^-126."""
+    v = (amax.astype(np.float32) / np.float32(448.0)).astype(np.float32)
+    m, e = np.frexp(v.astype(np.float64))           # v = m * 2^e, m in [0.5, 1)
+    s = np.where(m == 0.5, v.astype(np.float64), np.ldexp(1.0, e))
+    s = np.where(v == 0, 0.0, s)                     # frexp(0) = (0, 0): only the floor applies
+    return np.maximum(s, 2.0 ** -126).astype(np.float32)
+
+
+def test_pow2_golden_points(golden_dir):
+    rows = []
+    for line in open(os.path.join(golden_dir, "pow2_scale_points.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        first, rest, s_exp, code, _ = [f.strip() for f in line.split("|")]
+        rows.append((float(first), float(rest), float(s_exp), int(code, 16)))
+    x = np.array([[f] + [r] * 127 for f, r, _, _ in rows], np.float32)
+    q, s = oracle.cast_per_token(x, pow2=True)
+    for i, (_, _, s_exp, code) in enumerate(rows):
+        assert s[i, 0] == np.float32(s_exp), (i, s[i, 0], s_exp)
+        assert q[i, 0] == code, (i, hex(q[i, 0]), hex(code))
+
+
+def test_pow2_cast_matches_reading_and_encoder():
+    # s from numpy alone; q from the (separately pinned) encoder applied to the exact x / s
+    x = synth.with_outliers(synth.normal((96, 1024), 31, synth.TID_A), 31)
+    x[0, :128] = 0.0
+    x[1, :128] *= np.float32(1e-38)                 # s hits the 2^-126 floor
+    x[2, :128] *= np.float32(1e30)
+    q, s = oracle.cast_per_token(x, pow2=True)
+    amax = np.abs(x.reshape(96, 8, 128)).max(axis=2)
+    s_ref = _pow2_ceil_reference(amax)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+    assert ((s.view(np.uint32) & 0x7FFFFF) == 0).all()      # exact powers of two
+    y = (x.reshape(96, 8, 128) / s_ref[:, :, None]).astype(np.float32).reshape(96, 1024)
+    assert np.array_equal(q, oracle.encode(y))
+    # no code saturates: |x / s| <= 448 by construction
+    assert (np.abs(oracle.decode_table()[q]) <= 448).all()
+    # weights: the same rule over 128x128 blocks
+    w = synth.normal((256, 384), 32, synth.TID_B, std=0.02)
+    qb, sb = oracle.cast_per_block(w, pow2=True)
+    bmax = np.abs(w.reshape(2, 128, 3, 128)).max(axis=(1, 3))
+    assert np.array_equal(sb.view(np.uint32), _pow2_ceil_reference(bmax).view(np.uint32))
+
+
+def test_pow2_cast_power_of_two_invariance_is_exact():
+    # x -> 2^p x gives identical codes and s -> 2^p s exactly (no clamp or overflow in range)
+    x = synth.normal((32, 512), 33, synth.TID_A)
+    q0, s0 = oracle.cast_per_token(x, pow2=True)
+    for p in (-20, -3, 5, 40):
+        q1, s1 = oracle.cast_per_token((x * np.float32(2.0 ** p)).astype(np.float32), pow2=True)
+        assert np.array_equal(q0, q1)
+        assert np.array_equal(s1, (s0 * np.float32(2.0 ** p)).astype(np.float32))
+
+
 def test_bf16_input_is_widened_exactly():
     x = synth.normal((8, 256), 14, 1)
     bits = (x.view(np.uint32) >> 16).astype(np.uint16)
