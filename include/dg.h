@@ -62,6 +62,9 @@ typedef enum {
 
 typedef enum { DG_INPUT_F32 = 0, DG_INPUT_BF16 = 1 } dg_input_dtype_t;
 
+/* Scale format of a GEMM call: any fp32 values, or powers of two (UE8M0, see below). */
+typedef enum { DG_SCALE_F32 = 0, DG_SCALE_UE8M0 = 1 } dg_scale_format_t;
+
 /*
  * Per-token FP8 cast of activations (DeepSeek-V3 repo review, "Innovations" item 4:
  * one scale per 128 elements; "Risks" item 6: bound 448).
@@ -136,20 +139,48 @@ dg_status_t dg_grouped_gemm_masked(const uint8_t* a, const float* sfa, const uin
                                    int64_t expected_m, void* stream);
 
 /*
- * The three GEMMs above with the kernel schedule chosen by the caller (for tuning and
- * for tests that must cover every schedule on the same problem). Same math, same
- * arguments and same validation as the named entry points.
+ * Power-of-two (UE8M0) scales (DeepSeek-V3 repo review, "Innovations" item 4: V3.1's UE8M0
+ * format rounds every scale to a power of two, so that applying it is a shift).
+ *   The _ue8m0 casts are the casts above with s = the smallest power of two not below
+ *   fp32(amax / 448), and at least 2^-126; x / s is then exact. Same arguments, layouts
+ *   and errors; the scales are stored as fp32 (exact powers of two).
+ *   The _ue8m0 GEMMs compute the same D as the GEMMs above, with the same arguments,
+ *   layouts and errors, under the precondition that every sfa and sfb value is a power of
+ *   two in [2^-126, 2^127] (what the _ue8m0 casts produce). Where the shape allows, gfx950's
+ *   block-scaled MFMA then applies the scales itself and the products accumulate in its
+ *   fp32 accumulator, with no promotion on the vector ALUs. A scale that is not a power of
+ *   two gives unspecified output (not checked on the device).
+ */
+dg_status_t dg_cast_fp8_per_token_ue8m0(const void* x, dg_input_dtype_t x_dtype, int64_t G, int64_t M,
+                                        int64_t K, uint8_t* q, float* sf, void* stream);
+dg_status_t dg_cast_fp8_per_block_ue8m0(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K,
+                                        uint8_t* q, float* sf, void* stream);
+dg_status_t dg_gemm_fp8_nt_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                 uint16_t* d, int64_t M, int64_t N, int64_t K, void* stream);
+dg_status_t dg_grouped_gemm_contiguous_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                             const float* sfb, const int32_t* m_indices, uint16_t* d,
+                                             int32_t G, int64_t M_total, int64_t N, int64_t K, void* stream);
+dg_status_t dg_grouped_gemm_masked_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b,
+                                         const float* sfb, const int32_t* masked_m, uint16_t* d, int32_t G,
+                                         int64_t M_max, int64_t N, int64_t K, int64_t expected_m,
+                                         void* stream);
+
+/*
+ * The GEMMs above with the kernel schedule chosen by the caller (for tuning and for tests
+ * that must cover every schedule on the same problem). Same math, same arguments and same
+ * validation as the named entry points.
  *   layout:   0 = dense (meta ignored, G ignored), 1 = contiguous (meta = m_indices),
  *             2 = masked (meta = masked_m).
+ *   scale_fmt: DG_SCALE_F32, or DG_SCALE_UE8M0 with the precondition of the _ue8m0 GEMMs.
  *   schedule: 0 = automatic (what the named entry points use), 1 = decode (64-row
  *             blocks, K split over the waves of a workgroup; dense and masked only),
  *             2 = 128x128 LDS-staged tiles, 3 = 256x128 LDS-staged tiles (dense and
  *             masked only). A schedule a layout does not support falls back to 2.
  */
-dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, const uint8_t* a, const float* sfa,
-                                  const uint8_t* b, const float* sfb, const int32_t* meta, uint16_t* d,
-                                  int32_t G, int64_t M, int64_t N, int64_t K, int64_t expected_m,
-                                  void* stream);
+dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, int32_t scale_fmt, const uint8_t* a,
+                                  const float* sfa, const uint8_t* b, const float* sfb, const int32_t* meta,
+                                  uint16_t* d, int32_t G, int64_t M, int64_t N, int64_t K,
+                                  int64_t expected_m, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status_t status);

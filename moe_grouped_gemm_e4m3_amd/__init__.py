@@ -5,6 +5,9 @@ PyTorch supplies device memory and the current stream; FP8 tensors travel as tor
 (raw OCP E4M3FN bytes) and bf16 outputs as torch.bfloat16. There is no CPU fallback:
 if libdg.so is missing or fails to load, every call raises.
 
+Every entry point takes ue8m0=False; ue8m0=True selects the power-of-two (UE8M0) scale
+variants (the casts round each scale up to a power of two; the GEMMs require such scales).
+
 Activation scales are K-block-major ([K/128, M], leading [G] for the masked layout), as
 include/dg.h specifies; weight scales are [N/128, K/128].
 
@@ -30,6 +33,7 @@ DG_OK = 0
 STATUS_NAMES = {0: "DG_OK", 1: "DG_ERR_INVALID_ARGUMENT", 2: "DG_ERR_UNSUPPORTED_SHAPE",
                 3: "DG_ERR_MISALIGNED", 4: "DG_ERR_UNSUPPORTED_DEVICE", 5: "DG_ERR_LAUNCH"}
 LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+SCALE_F32, SCALE_UE8M0 = 0, 1
 SCHED_AUTO, SCHED_DECODE, SCHED_TILE128, SCHED_TILE256 = 0, 1, 2, 3
 INPUT_F32, INPUT_BF16 = 0, 1
 
@@ -52,15 +56,17 @@ def lib() -> ctypes.CDLL:
                               "or __graft_entry__.build()")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        L.dg_cast_fp8_per_token.argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, P]
-        L.dg_cast_fp8_per_block.argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
-        L.dg_gemm_fp8_nt.argtypes = [P, P, P, P, P, I64, I64, I64, P]
-        L.dg_grouped_gemm_contiguous.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
-        L.dg_grouped_gemm_masked.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
-        L.dg_gemm_fp8_scheduled.argtypes = [I32, I32, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
-        for fn in ("dg_cast_fp8_per_token", "dg_cast_fp8_per_block", "dg_gemm_fp8_nt",
-                   "dg_grouped_gemm_contiguous", "dg_grouped_gemm_masked", "dg_gemm_fp8_scheduled"):
-            getattr(L, fn).restype = ctypes.c_int
+        for sfx in ("", "_ue8m0"):
+            getattr(L, "dg_cast_fp8_per_token" + sfx).argtypes = [P, ctypes.c_int, I64, I64, I64, P, P, P]
+            getattr(L, "dg_cast_fp8_per_block" + sfx).argtypes = [P, ctypes.c_int, I64, I64, P, P, P]
+            getattr(L, "dg_gemm_fp8_nt" + sfx).argtypes = [P, P, P, P, P, I64, I64, I64, P]
+            getattr(L, "dg_grouped_gemm_contiguous" + sfx).argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+            getattr(L, "dg_grouped_gemm_masked" + sfx).argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+            for fn in ("dg_cast_fp8_per_token", "dg_cast_fp8_per_block", "dg_gemm_fp8_nt",
+                       "dg_grouped_gemm_contiguous", "dg_grouped_gemm_masked"):
+                getattr(L, fn + sfx).restype = ctypes.c_int
+        L.dg_gemm_fp8_scheduled.argtypes = [I32, I32, I32, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        L.dg_gemm_fp8_scheduled.restype = ctypes.c_int
         L.dg_status_string.argtypes = [ctypes.c_int]
         L.dg_status_string.restype = ctypes.c_char_p
         L.dg_last_error_message.argtypes = []
@@ -92,7 +98,8 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 
 # ---- casts ---------------------------------------------------------------------------
-def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None):
+def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
+                       ue8m0: bool = False):
     """x [M,K] or [G,M,K] fp32/bf16 -> (q uint8 e4m3 of x's shape, sf fp32 [K/128,M] or
     [G,K/128,M]: K-block-major, the sfa layout of the GEMMs)."""
     if x.dtype not in (torch.float32, torch.bfloat16):
@@ -108,11 +115,13 @@ def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch
     if tuple(q.shape) != tuple(x.shape) or tuple(sf.shape) != lead + (K // 128, M):
         raise ValueError("q %s / sf %s do not match x %s" % (tuple(q.shape), tuple(sf.shape), tuple(x.shape)))
     dt = INPUT_BF16 if x.dtype == torch.bfloat16 else INPUT_F32
-    _check(lib().dg_cast_fp8_per_token(_ptr(x), dt, G, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
+    fn = lib().dg_cast_fp8_per_token_ue8m0 if ue8m0 else lib().dg_cast_fp8_per_token
+    _check(fn(_ptr(x), dt, G, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
     return q, sf
 
 
-def cast_fp8_per_block(w: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None):
+def cast_fp8_per_block(w: torch.Tensor, q: torch.Tensor | None = None, sf: torch.Tensor | None = None,
+                       ue8m0: bool = False):
     """w [N,K] or [G,N,K] fp32/bf16 -> (q uint8 e4m3 same shape, sf [..., N/128, K/128] fp32)."""
     if w.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("w must be float32 or bfloat16")
@@ -125,7 +134,8 @@ def cast_fp8_per_block(w: torch.Tensor, q: torch.Tensor | None = None, sf: torch
     q = torch.empty(w.shape, dtype=torch.uint8, device=w.device) if q is None else q
     sf = torch.empty(lead + (N // 128, K // 128), dtype=torch.float32, device=w.device) if sf is None else sf
     dt = INPUT_BF16 if w.dtype == torch.bfloat16 else INPUT_F32
-    _check(lib().dg_cast_fp8_per_block(_ptr(w), dt, rows, K, _ptr(q), _ptr(sf), _stream(w.device)))
+    fn = lib().dg_cast_fp8_per_block_ue8m0 if ue8m0 else lib().dg_cast_fp8_per_block
+    _check(fn(_ptr(w), dt, rows, K, _ptr(q), _ptr(sf), _stream(w.device)))
     return q, sf
 
 
@@ -137,7 +147,7 @@ def _operands(a, sfa, b, sfb):
     _need(sfb, torch.float32, "sfb")
 
 
-def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = SCHED_AUTO):
+def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = SCHED_AUTO, ue8m0: bool = False):
     """a [M,K] e4m3, sfa [K/128,M], b [N,K] e4m3, sfb [N/128,K/128] -> d [M,N] bf16 = A * B^T."""
     _operands(a, sfa, b, sfb)
     M, K = a.shape
@@ -148,16 +158,18 @@ def gemm_fp8_nt(a, sfa, b, sfb, d: torch.Tensor | None = None, schedule: int = S
     d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
     _need(d, torch.bfloat16, "d")
     if schedule == SCHED_AUTO:
-        st = lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), M, N, K, _stream(a.device))
+        fn = lib().dg_gemm_fp8_nt_ue8m0 if ue8m0 else lib().dg_gemm_fp8_nt
+        st = fn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), M, N, K, _stream(a.device))
     else:
-        st = lib().dg_gemm_fp8_scheduled(LAYOUT_DENSE, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), None,
-                                         _ptr(d), 1, M, N, K, 0, _stream(a.device))
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_DENSE, schedule, SCALE_UE8M0 if ue8m0 else SCALE_F32, _ptr(a),
+                                         _ptr(sfa), _ptr(b), _ptr(sfb), None, _ptr(d), 1, M, N, K, 0,
+                                         _stream(a.device))
     _check(st)
     return d
 
 
 def grouped_gemm_contiguous(a, sfa, b, sfb, m_indices, d: torch.Tensor | None = None,
-                            schedule: int = SCHED_AUTO):
+                            schedule: int = SCHED_AUTO, ue8m0: bool = False):
     """a [M_total,K], sfa [K/128,M_total], b [G,N,K], sfb [G,N/128,K/128], m_indices [M_total]
     int32 (expert id or -1) -> d [M_total,N] bf16."""
     _operands(a, sfa, b, sfb)
@@ -170,17 +182,18 @@ def grouped_gemm_contiguous(a, sfa, b, sfb, m_indices, d: torch.Tensor | None = 
     d = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
     _need(d, torch.bfloat16, "d")
     if schedule == SCHED_AUTO:
-        st = lib().dg_grouped_gemm_contiguous(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d),
-                                              G, M, N, K, _stream(a.device))
+        fn = lib().dg_grouped_gemm_contiguous_ue8m0 if ue8m0 else lib().dg_grouped_gemm_contiguous
+        st = fn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d), G, M, N, K, _stream(a.device))
     else:
-        st = lib().dg_gemm_fp8_scheduled(LAYOUT_CONTIGUOUS, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb),
-                                         _ptr(m_indices), _ptr(d), G, M, N, K, 0, _stream(a.device))
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_CONTIGUOUS, schedule, SCALE_UE8M0 if ue8m0 else SCALE_F32,
+                                         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(m_indices), _ptr(d), G, M, N,
+                                         K, 0, _stream(a.device))
     _check(st)
     return d
 
 
 def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.Tensor | None = None,
-                        schedule: int = SCHED_AUTO):
+                        schedule: int = SCHED_AUTO, ue8m0: bool = False):
     """a [G,M_max,K], sfa [G,K/128,M_max], b [G,N,K], sfb [G,N/128,K/128], masked_m [G] int32
     -> d [G,M_max,N] bf16 (rows >= masked_m[g] are left untouched)."""
     _operands(a, sfa, b, sfb)
@@ -193,10 +206,12 @@ def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.
     d = torch.empty((G, M, N), dtype=torch.bfloat16, device=a.device) if d is None else d
     _need(d, torch.bfloat16, "d")
     if schedule == SCHED_AUTO:
-        st = lib().dg_grouped_gemm_masked(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d),
-                                          G, M, N, K, expected_m, _stream(a.device))
+        fn = lib().dg_grouped_gemm_masked_ue8m0 if ue8m0 else lib().dg_grouped_gemm_masked
+        st = fn(_ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d), G, M, N, K, expected_m,
+                _stream(a.device))
     else:
-        st = lib().dg_gemm_fp8_scheduled(LAYOUT_MASKED, schedule, _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb),
-                                         _ptr(masked_m), _ptr(d), G, M, N, K, expected_m, _stream(a.device))
+        st = lib().dg_gemm_fp8_scheduled(LAYOUT_MASKED, schedule, SCALE_UE8M0 if ue8m0 else SCALE_F32, _ptr(a),
+                                         _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(masked_m), _ptr(d), G, M, N, K,
+                                         expected_m, _stream(a.device))
     _check(st)
     return d

@@ -63,7 +63,7 @@ dg_status_t check_nk(int64_t N, int64_t K) {
 }
 
 // Common part of the three GEMM entry points.
-dg_status_t run_gemm(dg::Layout layout, int schedule, const uint8_t* a, const float* sfa, const uint8_t* b,
+dg_status_t run_gemm(dg::Layout layout, int schedule, bool pow2, const uint8_t* a, const float* sfa, const uint8_t* b,
                      const float* sfb, const int32_t* meta, uint16_t* d, int64_t G, int64_t M, int64_t N,
                      int64_t K, int64_t expected_m, void* stream, const char* name) {
   if (M < 0 || G < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
@@ -87,7 +87,7 @@ dg_status_t run_gemm(dg::Layout layout, int schedule, const uint8_t* a, const fl
   p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
   p.m_indices = layout == dg::Layout::Contiguous ? meta : nullptr;
   p.masked_m = layout == dg::Layout::Masked ? meta : nullptr;
-  p.M = M; p.N = N; p.K = K; p.G = (int32_t)G; p.layout = layout;
+  p.M = M; p.N = N; p.K = K; p.G = (int32_t)G; p.layout = layout; p.pow2 = pow2;
   const char* chosen = "";
   hipError_t e = dg::launch_gemm(p, static_cast<dg::Schedule>(schedule), expected_m,
                                  static_cast<hipStream_t>(stream), &chosen);
@@ -96,9 +96,10 @@ dg_status_t run_gemm(dg::Layout layout, int schedule, const uint8_t* a, const fl
   return launched(e, name);
 }
 
-dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int64_t groups, int64_t rows,
+dg_status_t run_cast(bool per_block, bool pow2, const void* x, dg_input_dtype_t dtype, int64_t groups, int64_t rows,
                      int64_t K, uint8_t* q, float* sf, void* stream) {
-  const char* name = per_block ? "dg_cast_fp8_per_block" : "dg_cast_fp8_per_token";
+  const char* name = per_block ? (pow2 ? "dg_cast_fp8_per_block_ue8m0" : "dg_cast_fp8_per_block")
+                               : (pow2 ? "dg_cast_fp8_per_token_ue8m0" : "dg_cast_fp8_per_token");
   if (dtype != DG_INPUT_F32 && dtype != DG_INPUT_BF16) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, (int)dtype);
   if (groups < 0 || rows < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
   if (K % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld is not a multiple of 128", name, (long long)K);
@@ -110,8 +111,9 @@ dg_status_t run_cast(bool per_block, const void* x, dg_input_dtype_t dtype, int6
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
   dg_status_t st = check_device();
   if (st != DG_OK) return st;
-  hipError_t e = per_block ? dg::launch_cast_per_block(x, dtype == DG_INPUT_BF16, rows, K, q, sf, static_cast<hipStream_t>(stream))
-                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, groups, rows, K, q, sf,
+  hipError_t e = per_block ? dg::launch_cast_per_block(x, dtype == DG_INPUT_BF16, pow2, rows, K, q, sf,
+                                                       static_cast<hipStream_t>(stream))
+                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, pow2, groups, rows, K, q, sf,
                                                        static_cast<hipStream_t>(stream));
   return launched(e, name);
 }
@@ -122,39 +124,72 @@ extern "C" {
 
 dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64_t G, int64_t M, int64_t K,
                                   uint8_t* q, float* sf, void* stream) {
-  return run_cast(false, x, x_dtype, G, M, K, q, sf, stream);
+  return run_cast(false, false, x, x_dtype, G, M, K, q, sf, stream);
 }
 
 dg_status_t dg_cast_fp8_per_block(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K, uint8_t* q,
                                   float* sf, void* stream) {
-  return run_cast(true, w, w_dtype, 1, N, K, q, sf, stream);
+  return run_cast(true, false, w, w_dtype, 1, N, K, q, sf, stream);
+}
+
+dg_status_t dg_cast_fp8_per_token_ue8m0(const void* x, dg_input_dtype_t x_dtype, int64_t G, int64_t M, int64_t K,
+                                        uint8_t* q, float* sf, void* stream) {
+  return run_cast(false, true, x, x_dtype, G, M, K, q, sf, stream);
+}
+
+dg_status_t dg_cast_fp8_per_block_ue8m0(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K, uint8_t* q,
+                                        float* sf, void* stream) {
+  return run_cast(true, true, w, w_dtype, 1, N, K, q, sf, stream);
 }
 
 dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
                            int64_t M, int64_t N, int64_t K, void* stream) {
-  return run_gemm(dg::Layout::Dense, 0, a, sfa, b, sfb, nullptr, d, 1, M, N, K, 0, stream, "dg_gemm_fp8_nt");
+  return run_gemm(dg::Layout::Dense, 0, false, a, sfa, b, sfb, nullptr, d, 1, M, N, K, 0, stream, "dg_gemm_fp8_nt");
 }
 
 dg_status_t dg_grouped_gemm_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                                        const int32_t* m_indices, uint16_t* d, int32_t G, int64_t M_total,
                                        int64_t N, int64_t K, void* stream) {
-  return run_gemm(dg::Layout::Contiguous, 0, a, sfa, b, sfb, m_indices, d, G, M_total, N, K, 0, stream,
+  return run_gemm(dg::Layout::Contiguous, 0, false, a, sfa, b, sfb, m_indices, d, G, M_total, N, K, 0, stream,
                   "dg_grouped_gemm_contiguous");
 }
 
 dg_status_t dg_grouped_gemm_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                                    const int32_t* masked_m, uint16_t* d, int32_t G, int64_t M_max, int64_t N,
                                    int64_t K, int64_t expected_m, void* stream) {
-  return run_gemm(dg::Layout::Masked, 0, a, sfa, b, sfb, masked_m, d, G, M_max, N, K, expected_m, stream,
+  return run_gemm(dg::Layout::Masked, 0, false, a, sfa, b, sfb, masked_m, d, G, M_max, N, K, expected_m, stream,
                   "dg_grouped_gemm_masked");
 }
 
-dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, const uint8_t* a, const float* sfa,
-                                  const uint8_t* b, const float* sfb, const int32_t* meta, uint16_t* d, int32_t G,
-                                  int64_t M, int64_t N, int64_t K, int64_t expected_m, void* stream) {
+dg_status_t dg_gemm_fp8_nt_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                                 int64_t M, int64_t N, int64_t K, void* stream) {
+  return run_gemm(dg::Layout::Dense, 0, true, a, sfa, b, sfb, nullptr, d, 1, M, N, K, 0, stream,
+                  "dg_gemm_fp8_nt_ue8m0");
+}
+
+dg_status_t dg_grouped_gemm_contiguous_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                             const int32_t* m_indices, uint16_t* d, int32_t G, int64_t M_total,
+                                             int64_t N, int64_t K, void* stream) {
+  return run_gemm(dg::Layout::Contiguous, 0, true, a, sfa, b, sfb, m_indices, d, G, M_total, N, K, 0, stream,
+                  "dg_grouped_gemm_contiguous_ue8m0");
+}
+
+dg_status_t dg_grouped_gemm_masked_ue8m0(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                                         const int32_t* masked_m, uint16_t* d, int32_t G, int64_t M_max, int64_t N,
+                                         int64_t K, int64_t expected_m, void* stream) {
+  return run_gemm(dg::Layout::Masked, 0, true, a, sfa, b, sfb, masked_m, d, G, M_max, N, K, expected_m, stream,
+                  "dg_grouped_gemm_masked_ue8m0");
+}
+
+dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, int32_t scale_fmt, const uint8_t* a,
+                                  const float* sfa, const uint8_t* b, const float* sfb, const int32_t* meta,
+                                  uint16_t* d, int32_t G, int64_t M, int64_t N, int64_t K, int64_t expected_m,
+                                  void* stream) {
   if (layout < 0 || layout > 2) return fail(DG_ERR_INVALID_ARGUMENT, "dg_gemm_fp8_scheduled: unknown layout %d", layout);
+  if (scale_fmt != DG_SCALE_F32 && scale_fmt != DG_SCALE_UE8M0)
+    return fail(DG_ERR_INVALID_ARGUMENT, "dg_gemm_fp8_scheduled: unknown scale format %d", scale_fmt);
   const dg::Layout L = static_cast<dg::Layout>(layout);
-  return run_gemm(L, schedule, a, sfa, b, sfb, L == dg::Layout::Dense ? nullptr : meta, d,
+  return run_gemm(L, schedule, scale_fmt == DG_SCALE_UE8M0, a, sfa, b, sfb, L == dg::Layout::Dense ? nullptr : meta, d,
                   L == dg::Layout::Dense ? 1 : G, M, N, K, expected_m, stream, "dg_gemm_fp8_scheduled");
 }
 

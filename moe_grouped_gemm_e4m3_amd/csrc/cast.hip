@@ -5,6 +5,9 @@
 // "Risks" 6: bound 448; DeepGEMM article, "FP8 and fine-grained scaling"):
 //   s = amax / 448, q = e4m3(x / s), both divisions correctly rounded fp32; round to
 //   nearest even with saturation; s == 0 gives signed zeros.
+// Power-of-two (UE8M0) variant (DeepSeek-V3 repo review, "Innovations" item 4: V3.1 rounds
+// the scales to powers of two so that scaling is a shift): s is the smallest power of two
+// not below amax / 448, and at least 2^-126; x / s is then exact.
 // Both kernels stream HBM: 4 B (fp32) or 2 B (bf16) read and ~1.03 B written per element.
 #include "dg_device.h"
 #include "dg_launch.h"
@@ -26,6 +29,15 @@ __device__ __forceinline__ void load4(const void* base, int64_t elem, float v[4]
   }
 }
 
+// The smallest power of two >= v, and >= 2^-126, from the fp32 bits: a normal v with a
+// zero mantissa is a power of two already; otherwise the exponent goes up by one.
+__device__ __forceinline__ float pow2_ceil(float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (b < 0x00800000u) return __uint_as_float(0x00800000u);  // 0, subnormal (v >= 0 here)
+  const uint32_t e = (b >> 23) + ((b & 0x007FFFFFu) ? 1u : 0u);
+  return __uint_as_float(e << 23);
+}
+
 __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
   uint32_t packed = 0;
 #pragma unroll
@@ -41,7 +53,7 @@ __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
 // the scale tensor [G][K/128][M] (row fastest): chunk c is row r = c % M, K block
 // kb = (c / M) % (K/128), group g = c / (M * K/128), so sf[c] is its own scale and the 8
 // scales of a pass are 32 contiguous bytes. Idx is uint32_t when the chunk count fits.
-template <bool kBf16, typename Idx>
+template <bool kBf16, bool kPow2, typename Idx>
 __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x, Idx nchunks,
                                                              Idx M, Idx kblocks, uint8_t* __restrict__ q,
                                                              float* __restrict__ sf) {
@@ -56,7 +68,7 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restr
     float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-    const float s = amax / 448.0f;
+    const float s = kPow2 ? pow2_ceil(amax / 448.0f) : amax / 448.0f;
     *reinterpret_cast<uint32_t*>(q + e0) = quant4(v, s);
     if (lane == 0) sf[c] = s;
   }
@@ -64,7 +76,7 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restr
 
 // One 256-thread block per 128x128 block. Thread t covers rows t/32 + 8*u (u = 0..15),
 // columns 4*(t%32) .. +3, so every pass of 256 threads reads 8 full 512-byte rows.
-template <bool kBf16>
+template <bool kBf16, bool kPow2>
 __global__ __launch_bounds__(256) void cast_per_block_kernel(const void* __restrict__ w,
                                                              int64_t K, int64_t kblocks,
                                                              uint8_t* __restrict__ q,
@@ -87,7 +99,7 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const void* __restr
   if ((t & 63) == 0) wave_max[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-  const float s = amax / 448.0f;
+  const float s = kPow2 ? pow2_ceil(amax / 448.0f) : amax / 448.0f;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int64_t row = bn * kQ + (t >> 5) + 8 * u;
@@ -96,10 +108,9 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const void* __restr
   if (t == 0) sf[bn * kblocks + bk] = s;
 }
 
-}  // namespace
-
-hipError_t launch_cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q,
-                                 float* sf, hipStream_t stream) {
+template <bool kPow2>
+hipError_t cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q, float* sf,
+                          hipStream_t stream) {
   const int64_t kblocks = K / kQ;
   const int64_t nchunks = G * M * kblocks;
   int64_t blocks = (nchunks + 7) / 8;
@@ -107,23 +118,36 @@ hipError_t launch_cast_per_token(const void* x, int bf16, int64_t G, int64_t M, 
   const dim3 grid((unsigned)blocks), block(256);
   if (nchunks < ((int64_t)1 << 32) - 8 * 8192) {  // c + one grid stride stays below 2^32
     const uint32_t n = (uint32_t)nchunks, m = (uint32_t)M, kbs = (uint32_t)kblocks;
-    if (bf16) cast_per_token_kernel<true, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
-    else cast_per_token_kernel<false, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
+    if (bf16) cast_per_token_kernel<true, kPow2, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
+    else cast_per_token_kernel<false, kPow2, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
   } else {
-    if (bf16) cast_per_token_kernel<true, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
-    else cast_per_token_kernel<false, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
+    if (bf16) cast_per_token_kernel<true, kPow2, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
+    else cast_per_token_kernel<false, kPow2, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_cast_per_block(const void* w, int bf16, int64_t N, int64_t K, uint8_t* q,
-                                 float* sf, hipStream_t stream) {
+template <bool kPow2>
+hipError_t cast_per_block(const void* w, int bf16, int64_t N, int64_t K, uint8_t* q, float* sf, hipStream_t stream) {
   const dim3 grid((unsigned)(N / kQ), (unsigned)(K / kQ));
   if (bf16)
-    cast_per_block_kernel<true><<<grid, dim3(256), 0, stream>>>(w, K, K / kQ, q, sf);
+    cast_per_block_kernel<true, kPow2><<<grid, dim3(256), 0, stream>>>(w, K, K / kQ, q, sf);
   else
-    cast_per_block_kernel<false><<<grid, dim3(256), 0, stream>>>(w, K, K / kQ, q, sf);
+    cast_per_block_kernel<false, kPow2><<<grid, dim3(256), 0, stream>>>(w, K, K / kQ, q, sf);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, int64_t M, int64_t K, uint8_t* q,
+                                 float* sf, hipStream_t stream) {
+  return pow2 ? cast_per_token<true>(x, bf16, G, M, K, q, sf, stream)
+              : cast_per_token<false>(x, bf16, G, M, K, q, sf, stream);
+}
+
+hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q,
+                                 float* sf, hipStream_t stream) {
+  return pow2 ? cast_per_block<true>(w, bf16, N, K, q, sf, stream) : cast_per_block<false>(w, bf16, N, K, q, sf, stream);
 }
 
 }  // namespace dg

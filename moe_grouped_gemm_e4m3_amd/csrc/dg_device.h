@@ -56,6 +56,14 @@ __device__ __forceinline__ v4f mfma_f8_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
+// c + 2^(ea-127) * 2^(eb-127) * (A . B) on the matrix unit (block-scaled form): ea is the
+// E8M0 scale this lane supplies for its A row (l & 15), eb the one for its B column; both
+// in byte 0 of the operand. The scale covers the 32 K values of the lane's group, so a
+// scale shared by a whole 128-K block is the same in every lane group.
+__device__ __forceinline__ v4f mfma_f8_16x16x128_scaled(const v8i& a, const v8i& b, const v4f& c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+}
+
 __device__ __forceinline__ v8i cat8(const v4i& lo, const v4i& hi) {
   v8i r;
   r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];

@@ -23,6 +23,7 @@ struct GemmProblem {
   int64_t M, N, K;
   int32_t G;
   Layout layout;
+  bool pow2;  // every sfa / sfb value is a power of two (UE8M0 scales)
 };
 
 // Kernel schedules. Decode: 64-row M blocks, K split across the waves of a workgroup,
@@ -32,9 +33,9 @@ enum class Schedule : int { Auto = 0, Decode = 1, Tile128 = 2, Tile256 = 3 };
 hipError_t launch_gemm(const GemmProblem& p, Schedule s, int64_t expected_m, hipStream_t stream,
                        const char** chosen);
 
-hipError_t launch_cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q,
+hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, int64_t M, int64_t K, uint8_t* q,
                                  float* sf, hipStream_t stream);
-hipError_t launch_cast_per_block(const void* w, int bf16, int64_t N, int64_t K, uint8_t* q, float* sf,
+hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q, float* sf,
                                  hipStream_t stream);
 
 }  // namespace dg

@@ -43,6 +43,7 @@ struct KParams {
   int G;
   int tiles_m, tiles_n;
   int nwg;
+  bool pow2;  // every scale is a power of two: the matrix unit applies them (where supported)
 };
 
 __device__ __forceinline__ int64_t clamp_rows(int64_t v, int64_t hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
@@ -58,14 +59,22 @@ __device__ __forceinline__ void lds_barrier() {
 // bytes [16i, 16i+16) (or [4i, 4i+4)) after the LDS base held in M0). They are issued from
 // inline assembly: they write only LDS and have no output registers; an address is a
 // wave-uniform 64-bit base plus a per-lane 32-bit offset. Waits for them are explicit.
+// Wave-uniform values in scalar registers; a no-op for values already there. The operands
+// below must be uniform, and the compiler cannot always prove that they are.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void lds_dma16(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff),
-               "s"(sbase)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff),
-               "s"(sbase)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds_base)),
+               "v"(voff), "s"(uniform_ptr(sbase))
                : "memory", "m0");
 }
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 //   3. The K-groups' partial tiles are summed in a fixed order through LDS (the bytes that
 //      held A) and written as bf16.
 // LDS: A [nkb][64 rows][128 B] | sa [nkb][64] fp32; afterwards the partial tiles.
-template <int BN, int KG, int KPW, int NW, Layout L>
+template <int BN, int KG, int KPW, int NW, Layout L, bool kPow2>
 __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
   static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
   constexpr int SG = NW / KG, TN = BN / 16 / SG;
@@ -259,7 +268,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
     for (int j = 0; j < TN; ++j) {
       const int64_t col = n0 + 16 * (sg * TN + j);
       bf[u][j] = load_frag_global(B + (col + fr) * K + (int64_t)kc * kQ + g4 * 16);
-      sbv[u][j] = SBg[(col / kQ) * nkb + kc] * (kb < nkb ? 1.0f : 0.0f);
+      sbv[u][j] = kPow2 ? SBg[(col / kQ) * nkb + kc] : SBg[(col / kQ) * nkb + kc] * (kb < nkb ? 1.0f : 0.0f);
     }
   }
   //    the activation block: instruction q covers rows 8*(q%8) .. +8 of K block q/8; lane l
@@ -294,6 +303,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
     const int kc = kb < nkb ? kb : nkb - 1;  // weight 0 past the end
     const uint8_t* ak = smem + kc * 8192 + fr * 128;
     const float* sk = reinterpret_cast<const float*>(smem + nkb * 8192 + kc * 256) + 4 * g4;
+    if constexpr (kPow2) {
+      // power-of-two scales, applied by the matrix unit (see the tile kernel); lane l gives
+      // the E8M0 scale of row 16i + (l & 15) and of its strip's weight block
+      if (kb < nkb) {
+        const uint32_t* ek = reinterpret_cast<const uint32_t*>(smem + nkb * 8192 + kc * 256) + fr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v8i af = cat8(*reinterpret_cast<const v4i*>(ak + i * 2048 + sw0),
+                              *reinterpret_cast<const v4i*>(ak + i * 2048 + sw1));
+          const int ea = (int)(ek[16 * i] >> 23);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = mfma_f8_16x16x128_scaled(af, bf[u][j], acc[i][j], ea, (int)(__float_as_uint(sbv[u][j]) >> 23));
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v8i af = cat8(*reinterpret_cast<const v4i*>(ak + i * 2048 + sw0),
@@ -968,7 +994,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
 // are staged in LDS up front), so the explicit vmcnt values count exactly those.
 constexpr int kMaxKb3 = 256;  // K blocks the direct-load tile kernel supports (K <= 32768)
 
-template <int BM, int BN, int WM, int WN, int STAGES, Layout L>
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1160,22 +1186,71 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     tt[1] = factor(s4[1], sb);
   };
 
+  // power-of-two scales: the matrix unit applies them. Lane l supplies the E8M0 scale of
+  // row l & 15 of the A strip (every lane group the same, the scale being per 128-K block)
+  // and of column l & 15 of the B strip; products accumulate straight into acc, with no
+  // promotion on the vector ALUs. An E8M0 byte is the fp32 exponent field of the scale.
+  const uint32_t e_lane = (uint32_t)((BM + BN) * kQ + (wm * WTM + fr) * 4);
+  auto read_a2 = [&](v8i& af, int& ea, int stage, int i) {
+    const uint8_t* st = smem + stage * STAGE_BYTES;
+    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw0),
+              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw1));
+    ea = (int)(*reinterpret_cast<const uint32_t*>(st + e_lane + 64 * i) >> 23);
+  };
+  auto kblock2 = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, int& e0) {
+    const int eb = (int)(__float_as_uint(sSB[wnb][kb]) >> 23);
+    v8i af[2];
+    int ea[2];
+    af[0] = a0;
+    ea[0] = e0;
+#pragma unroll
+    for (int i = 0; i < TM - 1; ++i) {
+      const int c = i & 1;
+      read_a2(af[c ^ 1], ea[c ^ 1], st, i + 1);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    lds_barrier();
+    issue(min(kb + STAGES, nkb - 1), st);  // past the end: a harmless reload
+    read_a2(a0, e0, sn, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb);
+    read_b(bf, sn);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
   // prologue: the first STAGES K blocks in flight; wait for K block 0
 #pragma unroll
   for (int q = 0; q < STAGES; ++q) issue(min(q, nkb - 1), q);
   wait_vmcnt<(STAGES - 1) * PER_STAGE>();
   lds_barrier();
   v8i bf[TN], a0;
-  float4 s0;
   read_b(bf, 0);
-  read_a(a0, s0, 0, 0);
   int st = 0;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int sn = st == STAGES - 1 ? 0 : st + 1;
-    kblock(kb, st, sn, bf, a0, s0);
-    st = sn;
+  if constexpr (kPow2) {
+    int e0;
+    read_a2(a0, e0, 0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int sn = st == STAGES - 1 ? 0 : st + 1;
+      kblock2(kb, st, sn, bf, a0, e0);
+      st = sn;
+    }
+  } else {
+    float4 s0;
+    read_a(a0, s0, 0, 0);
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int sn = st == STAGES - 1 ? 0 : st + 1;
+      kblock(kb, st, sn, bf, a0, s0);
+      st = sn;
+    }
+    promote(1, TM - 1);  // the last strip (odd slot)
   }
-  promote(1, TM - 1);  // the last strip (odd slot)
   wait_vmcnt<0>();     // drain the tail reloads before leaving
 
   // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
@@ -1218,7 +1293,10 @@ hipError_t run_tile3(KParams kp, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
-  gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+  if (kp.pow2)
+    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, true><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+  else
+    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, false><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -1338,7 +1416,7 @@ hipError_t run_decode_cfg(int bn, int nw, int kpw, const KParams& kp, hipStream_
   return hipSuccess;
 }
 
-template <int BN, int KG, int KPW, int NW, Layout L>
+template <int BN, int KG, int KPW, int NW, Layout L, bool kPow2>
 hipError_t run_decode2(KParams kp, hipStream_t s) {
   const size_t lds = decode2_need(BN, KG, kp.nkb);
   if (kp.N % BN != 0 || (int64_t)KG * KPW < kp.nkb || lds > kLdsBytes || 64 * kp.K >= ((int64_t)1 << 32))
@@ -1349,10 +1427,10 @@ hipError_t run_decode2(KParams kp, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode2_kernel<BN, KG, KPW, NW, L>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode2_kernel<BN, KG, KPW, NW, L, kPow2>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
   if (attr != hipSuccess) return attr;
-  gemm_decode2_kernel<BN, KG, KPW, NW, L><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
+  gemm_decode2_kernel<BN, KG, KPW, NW, L, kPow2><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -1366,8 +1444,9 @@ hipError_t run_decode2(KParams kp, hipStream_t s) {
 
 template <Layout L>
 hipError_t run_decode2_cfg(int bn, int kg, int kpw, int nw, const KParams& kp, hipStream_t s) {
-#define DG_X(a, b, c, d) \
-  if (bn == a && kg == b && kpw == c && nw == d) return run_decode2<a, b, c, d, L>(kp, s);
+#define DG_X(a, b, c, d)                                                                     \
+  if (bn == a && kg == b && kpw == c && nw == d)                                           \
+    return kp.pow2 ? run_decode2<a, b, c, d, L, true>(kp, s) : run_decode2<a, b, c, d, L, false>(kp, s);
   DG_DECODE2_CONFIGS(DG_X)
 #undef DG_X
   return hipErrorNotSupported;
@@ -1461,7 +1540,7 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   KParams kp{};
   kp.a = p.a; kp.sfa = p.sfa; kp.b = p.b; kp.sfb = p.sfb; kp.d = p.d;
   kp.m_indices = p.m_indices; kp.masked_m = p.masked_m;
-  kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G;
+  kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G; kp.pow2 = p.pow2;
 
   if (sched == Schedule::Auto) {
     if (p.layout == Layout::Dense)

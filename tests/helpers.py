@@ -33,10 +33,10 @@ def bf16_values(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def gpu_cast_tokens(dg, a_f32: np.ndarray):
+def gpu_cast_tokens(dg, a_f32: np.ndarray, ue8m0: bool = False):
     """Per-token cast on the GPU of [M,K] or [G,M,K]; returns device (q, sf) with sf in the
     library's K-block-major layout ([K/128,M] or [G,K/128,M])."""
-    return dg.cast_fp8_per_token(to_dev(a_f32))
+    return dg.cast_fp8_per_token(to_dev(a_f32), ue8m0=ue8m0)
 
 
 def kmajor(s: np.ndarray) -> np.ndarray:
@@ -44,8 +44,8 @@ def kmajor(s: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.swapaxes(s, -1, -2))
 
 
-def gpu_cast_blocks(dg, w_f32: np.ndarray):
-    return dg.cast_fp8_per_block(to_dev(w_f32))
+def gpu_cast_blocks(dg, w_f32: np.ndarray, ue8m0: bool = False):
+    return dg.cast_fp8_per_block(to_dev(w_f32), ue8m0=ue8m0)
 
 
 def oracle_cast_tokens(a_f32: np.ndarray):
@@ -76,14 +76,14 @@ def assert_close(y: np.ndarray, R: np.ndarray, what: str, mask=None) -> dict:
     return res
 
 
-def quantised_dense(dg, M, N, K, seed=0, outliers=False):
+def quantised_dense(dg, M, N, K, seed=0, outliers=False, ue8m0=False):
     """Seeded fp32 inputs, quantised by both sides; byte/bit equality of the casts asserted.
     Returns (device q/s tensors, oracle q/s arrays)."""
     a, b = synth.dense_inputs(M, N, K, seed, outliers)
-    qa_d, sa_d = gpu_cast_tokens(dg, a)
-    qb_d, sb_d = gpu_cast_blocks(dg, b)
-    qa, sa = oracle.cast_per_token(a)
-    qb, sb = oracle.cast_per_block(b)
+    qa_d, sa_d = gpu_cast_tokens(dg, a, ue8m0)
+    qb_d, sb_d = gpu_cast_blocks(dg, b, ue8m0)
+    qa, sa = oracle.cast_per_token(a, pow2=ue8m0)
+    qb, sb = oracle.cast_per_block(b, pow2=ue8m0)
     assert_same_bytes(qa_d, qa, "A cast %dx%d" % (M, K))
     assert_same_bits(sa_d, kmajor(sa), "A scales %dx%d" % (M, K))
     assert_same_bytes(qb_d, qb, "B cast %dx%d" % (N, K))

@@ -86,8 +86,12 @@ def test_grouped_argument_errors(L):
     assert m(P, P, P, P, None, P, 4, 64, 256, 512, 0, None) == 1
     assert m(P, P, P, P, Q, P, 4, 64, 256, 512, 0, None) == 3
     s = L.dg_gemm_fp8_scheduled
-    assert s(7, 0, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
-    assert s(0, 9, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
+    assert s(7, 0, 0, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
+    assert s(0, 9, 0, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1
+    assert s(0, 0, 5, P, P, P, P, P, P, 1, 64, 256, 512, 0, None) == 1  # unknown scale format
+    u = L.dg_gemm_fp8_nt_ue8m0
+    assert u(P, P, P, P, P, 64, 256, 500, None) == 2
+    assert u(P, P, P, P, P, 0, 256, 512, None) == 0
 
 
 def test_cast_argument_errors(L):
