@@ -218,11 +218,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode_kernel(KParams p) {
 // Workgroup: 64 rows x BN columns over all of K, NW waves = KG K-groups x (NW/KG) column
 // groups. Every weight byte is read once; the 64 x K activation block is read once per
 // workgroup, straight into LDS with full-line direct loads, instead of once per wave.
-//   1. Each wave issues all its B fragment loads (K blocks kg, kg+KG, ... of its TN strips)
-//      and weight scales, then its share of the activation block and its scales (direct
-//      loads into LDS), then waits for everything and joins a barrier.
-//   2. Per K block: A fragments from LDS (16-byte chunks XOR-swizzled by row), 4 x TN
-//      MFMAs, promotion by sa * sb.
+//   1. Each wave issues its share of the activation block and its scales (direct loads
+//      into LDS), then all its B fragment loads (K blocks kg, kg+KG, ... of its TN strips)
+//      and weight scales; it waits for its share of A only and joins a barrier.
+//   2. Per K block, as its B fragments arrive: A fragments from LDS (16-byte chunks
+//      XOR-swizzled by row), 4 x TN MFMAs, promotion by sa * sb.
 //   3. The K-groups' partial tiles are summed in a fixed order through LDS (the bytes that
 //      held A) and written as bf16.
 // LDS: A [nkb][64 rows][128 B] | sa [nkb][64] fp32; afterwards the partial tiles.
@@ -256,9 +256,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
   const int fr = l & 15, g4 = l >> 4;
   const int rows = (int)(valid - m0 < 64 ? valid - m0 : 64);  // rows >= this are clamped
 
-  // 1. B fragments and weight scales of this wave's K blocks (a K block past the end
-  //    reloads the last one with weight 0)
-  v8i bf[KPW][TN];
+  // 1. the weight scales of this wave's K blocks (a K block past the end reloads the last
+  //    one, with weight 0); then the activation block and its scales, straight into LDS:
+  //    instruction q covers rows 8*(q%8) .. +8 of K block q/8, and lane l fetches chunk
+  //    (l&7) ^ (row&7) of its row, so LDS holds the swizzled layout; then the B fragments
   float sbv[KPW][TN];
 #pragma unroll
   for (int u = 0; u < KPW; ++u) {
@@ -267,12 +268,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t col = n0 + 16 * (sg * TN + j);
-      bf[u][j] = load_frag_global(B + (col + fr) * K + (int64_t)kc * kQ + g4 * 16);
       sbv[u][j] = kPow2 ? SBg[(col / kQ) * nkb + kc] : SBg[(col / kQ) * nkb + kc] * (kb < nkb ? 1.0f : 0.0f);
     }
   }
-  //    the activation block: instruction q covers rows 8*(q%8) .. +8 of K block q/8; lane l
-  //    fetches chunk (l&7) ^ (row&7) of its row so that LDS holds the swizzled layout
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
   {
     const int row = (l >> 3);  // + 8 * (q % 8)
@@ -287,8 +285,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
     for (int kb = w; kb < nkb; kb += NW)
       lds_dma4(soff, SA + (int64_t)kb * p.M, sbase + (uint32_t)(nkb * 8192 + kb * 256));
   }
-  wait_vmcnt<0>();
-  __syncthreads();
+  v8i bf[KPW][TN];
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int kb = kg + KG * u;
+    const int kc = kb < nkb ? kb : nkb - 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + 16 * (sg * TN + j);
+      bf[u][j] = load_frag_global(B + (col + fr) * K + (int64_t)kc * kQ + g4 * 16);
+    }
+  }
+  //    Loads complete in issue order, and the 2*KPW*TN B fragment loads were issued after
+  //    the direct ones: at most that many outstanding means this wave's share of A is in
+  //    LDS. The barrier then covers every wave's share; the B fragments keep
+  //    arriving while the first K blocks are computed.
+  wait_vmcnt<2 * KPW * TN>();
+  lds_barrier();
 
   // 2. MFMAs per K block, promotion by sa * sb
   v4f acc[4][TN];
@@ -336,45 +349,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
     }
   }
 
-  // 3. K-group partials: groups 1.. store their fragments (lane-native order), group 0
-  //    adds them in order kg = 1, 2, ... and stores the sum row-major for the bf16 pass
+  // 3. every wave stores its partial tile row-major in LDS (the bytes that held A); then
+  //    each thread sums the KG partials of 4 consecutive columns in the fixed order kg = 0,
+  //    1, ... and writes them as bf16
   __syncthreads();  // every wave is done with A in LDS
-  float4* part = reinterpret_cast<float4*>(smem);
-  constexpr int FR = 4 * TN * 64;  // float4 per partial tile of one wave
-  if (kg > 0) {
+  float* part = reinterpret_cast<float*>(smem);  // [KG][64][BN]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        part[((kg - 1) * SG + sg) * FR + (i * TN + j) * 64 + l] =
-            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-  }
-  __syncthreads();
-  float* tile = reinterpret_cast<float*>(part + (KG - 1) * SG * FR);  // [64][BN]
-  if (kg == 0) {
-    for (int k2 = 1; k2 < KG; ++k2) {
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float4 v = part[((k2 - 1) * SG + sg) * FR + (i * TN + j) * 64 + l];
-          acc[i][j][0] += v.x; acc[i][j][1] += v.y; acc[i][j][2] += v.z; acc[i][j][3] += v.w;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) tile[(16 * i + 4 * g4 + r) * BN + 16 * (sg * TN + j) + fr] = acc[i][j][r];
-  }
+      for (int r = 0; r < 4; ++r)
+        part[(kg * 64 + 16 * i + 4 * g4 + r) * BN + 16 * (sg * TN + j) + fr] = acc[i][j][r];
   __syncthreads();
   constexpr int kGroups = 64 * BN / 4;  // 4 consecutive columns per thread-step
   for (int e = t; e < kGroups; e += 64 * NW) {
     const int row = e / (BN / 4);
     const int c4 = (e % (BN / 4)) * 4;
     if (row < rows) {
-      const float4 v = *reinterpret_cast<const float4*>(&tile[row * BN + c4]);
+      float4 v = *reinterpret_cast<const float4*>(&part[row * BN + c4]);
+#pragma unroll
+      for (int k2 = 1; k2 < KG; ++k2) {
+        const float4 u4 = *reinterpret_cast<const float4*>(&part[(k2 * 64 + row) * BN + c4]);
+        v.x += u4.x; v.y += u4.y; v.z += u4.z; v.w += u4.w;
+      }
       uint2 o;
       o.x = bf16_rne(v.x) | (bf16_rne(v.y) << 16);
       o.y = bf16_rne(v.z) | (bf16_rne(v.w) << 16);
@@ -384,8 +382,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_decode2_kernel(KParams p) {
 }
 
 inline size_t decode2_need(int bn, int kg, int nkb) {  // bytes of dynamic LDS
-  const size_t a = (size_t)nkb * 8192 + (size_t)nkb * 256;             // A block + its scales
-  const size_t r = (size_t)(kg - 1) * 64 * bn * 4 + (size_t)64 * bn * 4;  // partial tiles + sum
+  const size_t a = (size_t)nkb * 8192 + (size_t)nkb * 256;  // A block + its scales
+  const size_t r = (size_t)kg * 64 * bn * 4;                 // the K-groups' partial tiles
   return a > r ? a : r;
 }
 
