@@ -1091,9 +1091,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 
   const int fr = l & 15, g4 = l >> 4;
   const uint32_t sw0 = (uint32_t)((g4 ^ (fr & 7)) << 4), sw1 = (uint32_t)(((g4 + 4) ^ (fr & 7)) << 4);
-  const uint32_t a_lane = (uint32_t)((wm * WTM + fr) * kQ);
+  // strip i of wave row wm holds rows (i * WM + wm) * 16 .. +16 of the tile: the wave rows
+  // interleave by strips, so a partly valid tile (masked layout) leaves every wave a
+  // similar number of active strips
+  const uint32_t a_lane = (uint32_t)((wm * 16 + fr) * kQ);
   const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * WTN + fr) * kQ);
-  const uint32_t s_lane = (uint32_t)((BM + BN) * kQ + (wm * WTM + 4 * g4) * 4);
+  const uint32_t s_lane = (uint32_t)((BM + BN) * kQ + (wm * 16 + 4 * g4) * 4);
   const int wnb = (wn * WTN) / (int)kQ;  // this wave's weight-scale column block
 
   auto read_b = [&](v8i (&bf)[TN], int stage) {
@@ -1105,9 +1108,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   };
   auto read_a = [&](v8i& af, float4& s4, int stage, int i) {
     const uint8_t* st = smem + stage * STAGE_BYTES;
-    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw0),
-              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw1));
-    s4 = *reinterpret_cast<const float4*>(st + s_lane + 64 * i);
+    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * WM * kQ + sw0),
+              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * WM * kQ + sw1));
+    s4 = *reinterpret_cast<const float4*>(st + s_lane + 64 * WM * i);
   };
 
   v4f pp[2][TN];
@@ -1118,7 +1121,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) pp[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
+  // masked layout: strips wholly beyond the valid rows skip their MFMAs and promotions
+  // (their rows are never stored); act is wave-uniform
+  int act = TM;
+  if constexpr (L == Layout::Masked) {
+    const int64_t left = valid - m0 - wm * 16;  // rows from this wave's first strip on
+    act = left <= 0 ? 0 : (int)min((int64_t)TM, (left + 16 * WM - 1) / (16 * WM));
+  }
   auto promote = [&](int slot, int strip) {
+    if (L == Layout::Masked && strip >= act) return;
     const float4 tp = tt[slot];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -1133,9 +1144,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     for (int j = 0; j < TN; ++j) asm volatile("" ::"v"(acc[strip][j]));
   };
   // MFMAs of one strip into `slot`, interleaved with the promotion of the other slot
-  auto strip = [&](const v8i& af, const v8i (&bf)[TN], int slot, int prev_strip) {
+  auto strip = [&](const v8i& af, const v8i (&bf)[TN], int slot, int cur_strip, int prev_strip) {
+    if (!(L == Layout::Masked && cur_strip >= act)) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) pp[slot][j] = mfma_f8_16x16x128(af, bf[j]);
+      for (int j = 0; j < TN; ++j) pp[slot][j] = mfma_f8_16x16x128(af, bf[j]);
+    }
     promote(slot ^ 1, prev_strip);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -1160,7 +1173,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     for (int i = 0; i < TM - 1; ++i) {
       const int c = i & 1;
       read_a(af[c ^ 1], s4[c ^ 1], st, i + 1);
-      strip(af[c], bf, c, i == 0 ? TM - 1 : i - 1);  // strip 0 promotes the previous K block's last
+      strip(af[c], bf, c, i, i == 0 ? TM - 1 : i - 1);  // strip 0 promotes the previous K block's last
       tt[c] = factor(s4[c], sb);
     }
     // every read of stage st is issued; wait for the next stage, then recycle stage st
@@ -1172,7 +1185,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     // last strip (odd slot): B fragment j is reloaded from stage sn right after the MFMA
     // that last reads it
 #pragma unroll
-    for (int j = 0; j < TN; ++j) pp[1][j] = mfma_f8_16x16x128(af[1], bf[j]);
+    for (int j = 0; j < TN; ++j)
+      if (!(L == Layout::Masked && TM - 1 >= act)) pp[1][j] = mfma_f8_16x16x128(af[1], bf[j]);
     promote(0, TM - 2);
     read_b(bf, sn);
 #pragma unroll
@@ -1188,12 +1202,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   // row l & 15 of the A strip (every lane group the same, the scale being per 128-K block)
   // and of column l & 15 of the B strip; products accumulate straight into acc, with no
   // promotion on the vector ALUs. An E8M0 byte is the fp32 exponent field of the scale.
-  const uint32_t e_lane = (uint32_t)((BM + BN) * kQ + (wm * WTM + fr) * 4);
+  const uint32_t e_lane = (uint32_t)((BM + BN) * kQ + (wm * 16 + fr) * 4);
   auto read_a2 = [&](v8i& af, int& ea, int stage, int i) {
     const uint8_t* st = smem + stage * STAGE_BYTES;
-    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw0),
-              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * kQ + sw1));
-    ea = (int)(*reinterpret_cast<const uint32_t*>(st + e_lane + 64 * i) >> 23);
+    af = cat8(*reinterpret_cast<const v4i*>(st + a_lane + i * 16 * WM * kQ + sw0),
+              *reinterpret_cast<const v4i*>(st + a_lane + i * 16 * WM * kQ + sw1));
+    ea = (int)(*reinterpret_cast<const uint32_t*>(st + e_lane + 64 * WM * i) >> 23);
   };
   auto kblock2 = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, int& e0) {
     const int eb = (int)(__float_as_uint(sSB[wnb][kb]) >> 23);
@@ -1206,7 +1220,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       const int c = i & 1;
       read_a2(af[c ^ 1], ea[c ^ 1], st, i + 1);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
+      for (int j = 0; j < TN; ++j)
+        if (!(L == Layout::Masked && i >= act)) acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -1214,7 +1229,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     issue(min(kb + STAGES, nkb - 1), st);  // past the end: a harmless reload
     read_a2(a0, e0, sn, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb);
+    for (int j = 0; j < TN; ++j)
+      if (!(L == Layout::Masked && TM - 1 >= act))
+        acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb);
     read_b(bf, sn);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -1256,7 +1273,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm * WTM + 16 * i + 4 * g4 + r;
+      const int64_t row = m0 + (i * WM + wm) * 16 + 4 * g4 + r;
       if (row < valid) {
         uint16_t* drow = D + row * p.N + n0 + wn * WTN + fr;
 #pragma unroll
@@ -1604,6 +1621,11 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         if (is("t3_128x256")) {
           pick("tile3_128x256");
           const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Masked>(kp, stream);
+          if (e != hipErrorNotSupported) return e;
+        }
+        if (is("t3_256x128")) {
+          pick("tile3_256x128");
+          const hipError_t e = run_tile3<256, 128, 4, 2, 3, Layout::Masked>(kp, stream);
           if (e != hipErrorNotSupported) return e;
         }
         pick("tile3_256x256");
