@@ -17,6 +17,7 @@ of the same workload. `traffic` (HBM bytes per launch) is read from profiles/tra
 when that file was produced from the current kernel source.
 
 Other workloads (--workload prefill|contiguous|masked|tiny) print the same line shape.
+--ue8m0 runs the same steps with power-of-two (UE8M0) scales: the _ue8m0 casts and GEMMs.
 """
 from __future__ import annotations
 
@@ -70,7 +71,7 @@ def cast_bytes(rows, K):
     return float(rows * K * 4 + rows * K + 4 * rows * K // 128)
 
 
-def build_layer(dg, torch, kind, s, seed, copies):
+def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
     """Device inputs for one layer: fp32 activations, `copies` quantised weight copies."""
     import numpy as np
     import synth
@@ -106,7 +107,7 @@ def build_layer(dg, torch, kind, s, seed, copies):
     ws = []
     for c in range(copies):
         w = torch.randn((G * N, K), generator=gen, device=dev, dtype=torch.float32) * 0.02
-        qb, sb = dg.cast_fp8_per_block(w)
+        qb, sb = dg.cast_fp8_per_block(w, ue8m0=ue8m0)
         del w
         if kind == "dense":
             ws.append((qb, sb))
@@ -119,7 +120,7 @@ def build_layer(dg, torch, kind, s, seed, copies):
         d = torch.empty((s["G"], s["M_max"], N), dtype=torch.bfloat16, device=dev)
     else:
         d = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
-    return dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G)
+    return dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G, ue8m0=ue8m0)
 
 
 def run_layer(dg, L, copy_idx):
@@ -127,14 +128,15 @@ def run_layer(dg, L, copy_idx):
     kind, s = L["kind"], L["s"]
     K = s["K"]
     qb, sb = L["ws"][copy_idx % len(L["ws"])]
-    dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"])
+    u = L["ue8m0"]
+    dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=u)
     if kind == "dense":
-        dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"])
+        dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"], ue8m0=u)
     elif kind == "contiguous":
-        dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
+        dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"], ue8m0=u)
     else:
         dg.grouped_gemm_masked(L["qa"], L["sa"], qb, sb, L["meta"], expected_m=max(1, L["valid"] // L["G"]),
-                               d=L["d"])
+                               d=L["d"], ue8m0=u)
 
 
 def load_traffic(workload, label):
@@ -153,7 +155,7 @@ def load_traffic(workload, label):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(workload, budget_s):
+def cpu_baseline(workload, budget_s, ue8m0=False):
     """The CPU oracle (unchanged) on a bounded sample of the workload: every layer's cast
     and GEMM over a row sample, repeated until ~budget_s seconds of work."""
     import numpy as np
@@ -169,7 +171,7 @@ def cpu_baseline(workload, budget_s):
         G = s.get("G", 1)
         bcols = N if kind == "dense" and N * K * rows <= 2 ** 31 else min(N, 2048)
         b = synth.normal((bcols, K), li, synth.TID_B, 0.02)
-        qb, sb = oracle.cast_per_block(b)
+        qb, sb = oracle.cast_per_block(b, pow2=ue8m0)
         jobs.append((a, qb, sb, rows, bcols, K))
         sample_desc.append("%dx%dx%d" % (rows, bcols, K))
     flops = 0.0
@@ -177,7 +179,7 @@ def cpu_baseline(workload, budget_s):
     reps = 0
     while True:
         for a, qb, sb, rows, bcols, K in jobs:
-            qa, sa = oracle.cast_per_token(a)
+            qa, sa = oracle.cast_per_token(a, pow2=ue8m0)
             oracle.gemm(qa, sa, qb, sb)
             flops += 2.0 * rows * bcols * K
         reps += 1
@@ -226,6 +228,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ue8m0", action="store_true", help="power-of-two (UE8M0) scales")
     ap.add_argument("--kernel-reps", type=int, default=0,
                     help="launches per kernel in the per-kernel timing (default: steps)")
     ap.add_argument("--cache-bytes", type=float, default=512 * 2 ** 20,
@@ -250,7 +253,8 @@ def main():
     # weight copies so each step streams its weights from HBM, not the 256 MiB cache
     wbytes = sum(s.get("G", 1) * s["N"] * s["K"] for _, s in wl["layers"])
     copies = int(min(64, max(1, math.ceil(args.cache_bytes / wbytes))))
-    layers = [build_layer(dg, torch, kind, s, args.seed + i, copies) for i, (kind, s) in enumerate(wl["layers"])]
+    layers = [build_layer(dg, torch, kind, s, args.seed + i, copies, args.ue8m0)
+              for i, (kind, s) in enumerate(wl["layers"])]
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -287,17 +291,18 @@ def main():
         N, K = s_["N"], s_["K"]
 
         def cast_only(L=L):
-            dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"])
+            dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
 
         def gemm_only(c, L=L):
             qb, sb = L["ws"][c % len(L["ws"])]
+            u = L["ue8m0"]
             if L["kind"] == "dense":
-                dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"])
+                dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"], ue8m0=u)
             elif L["kind"] == "contiguous":
-                dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"])
+                dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"], ue8m0=u)
             else:
                 dg.grouped_gemm_masked(L["qa"], L["sa"], qb, sb, L["meta"],
-                                       expected_m=max(1, L["valid"] // L["G"]), d=L["d"])
+                                       expected_m=max(1, L["valid"] // L["G"]), d=L["d"], ue8m0=u)
 
         g_cast = capture(torch, lambda: [cast_only() for _ in range(copies)])
         g_gemm = capture(torch, lambda: [gemm_only(c) for c in range(copies)])
@@ -320,7 +325,7 @@ def main():
         achieved, peak, unit = dom["gbs"], PEAK_HBM_GBS, "GB/s"
     else:
         achieved, peak, unit = dom["tflops"], PEAK_FP8_TFLOPS, "TFLOP/s"
-    traffic = load_traffic(args.workload, dom["layer"] + " " + dom["kernel"])
+    traffic = load_traffic(args.workload + ("_ue8m0" if args.ue8m0 else ""), dom["layer"] + " " + dom["kernel"])
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     out = {
@@ -328,6 +333,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": wl["desc"], "weight_copies": copies,
+                   "scales": "UE8M0 (powers of two)" if args.ue8m0 else "fp32 (amax / 448)",
                    "step": "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM (bf16 out), "
                            "per layer; replayed from HIP graphs"},
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5),
@@ -338,7 +344,7 @@ def main():
         "kernels": [{k: (round(v, 3) if isinstance(v, float) else v) for k, v in kk.items()} for kk in kernels],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_budget, args.ue8m0)
         out["cpu_baseline"]["value"] = round(out["cpu_baseline"]["value"], 6)
     print(json.dumps(out), flush=True)
 
