@@ -14,6 +14,9 @@ Method source (cited by page title and section):
     FP8 products over a K stretch are promoted to fp32 and accumulated.
   * DeepSeek-V3 repo review, "Innovations" 4 and "Risks" 6: one scale per 128
     elements, 128x128 weight blocks, quantisation bound 448.
+  * DeepGEMM article, "swapAB and Mega MoE": the expert FFN, two grouped GEMMs with the
+    SwiGLU activation between them (moe_ffn_contiguous / moe_ffn_masked compose the
+    GEMM and cast oracles with an fp64 SwiGLU; readings stated beside them).
 """
 from __future__ import annotations
 
@@ -245,3 +248,71 @@ def compare(y, R, mask=None) -> dict:
     return {"ok": bool(ok), "n_bad": int(bad.sum()), "count": int(Rs.size),
             "worst_excess": float(np.nanmax(excess)) if excess.size else 0.0,
             "sim": float(sim), "rms": rms}
+
+
+# ---- MoE expert FFN: gate/up GEMM -> SwiGLU -> per-token FP8 re-cast -> down GEMM ----------
+# DeepGEMM article, section "swapAB and Mega MoE": the expert FFN runs two grouped GEMMs with
+# the SwiGLU activation between them. Readings (the pages give no formulas for this part):
+#   * the first weight tensor is [G, 2I, H]: rows [0, I) are the gate projection, rows
+#     [I, 2I) the up projection; the second is [G, H, I] (the down projection);
+#   * SwiGLU(g, u) = silu(g) * u with silu(x) = x * sigmoid(x), evaluated on the fp64 GEMM
+#     results (no bf16 rounding of the gate/up outputs in between);
+#   * the activation h is materialised in fp32 and cast to FP8 with the per-token rule
+#     (1x128 chunks along I, s = amax / 448 or its power-of-two form); the down GEMM takes
+#     those bytes and scales like any other activation;
+#   * rows that belong to no expert (contiguous padding, masked rows >= masked_m) are not
+#     part of the result (NaN here).
+def silu(x) -> np.ndarray:
+    """x * sigmoid(x) = x / (1 + exp(-x)) in fp64 (exp overflow for very negative x gives -0)."""
+    x = np.asarray(x, np.float64)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def swiglu(gate_up) -> np.ndarray:
+    """[..., 2I] -> [..., I]: silu(gate) * up, the gate being the first I columns."""
+    gate_up = np.asarray(gate_up, np.float64)
+    I = gate_up.shape[-1] // 2
+    assert gate_up.shape[-1] == 2 * I
+    return silu(gate_up[..., :I]) * gate_up[..., I:]
+
+
+def _recast_rows(h: np.ndarray, valid: np.ndarray, pow2: bool):
+    """Per-token cast of h [R, I] on its valid rows (others are cast as zeros and then
+    marked NaN in the scales)."""
+    h32 = np.where(valid[:, None], h, 0.0).astype(np.float32)
+    hq, sh = cast_per_token(h32, pow2)
+    sh = sh.copy()
+    sh[~valid] = np.nan
+    return h32, hq, sh
+
+
+def moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, m_indices, pow2: bool = False) -> dict:
+    """Expert FFN in the contiguous layout. xq [M_total,H] codes with sx [M_total,H/128];
+    w1q [G,2I,H] with s1 [G,2I/128,H/128]; w2q [G,H,I] with s2 [G,H/128,I/128];
+    m_indices [M_total]. Returns gate_up [M_total,2I], h [M_total,I] (fp64), h32 (fp32),
+    hq [M_total,I] codes and sh [M_total,I/128] (the re-cast), y [M_total,H] (fp64);
+    padding rows are NaN in gate_up, h, sh and y."""
+    gu = grouped_contiguous(xq, sx, w1q, s1, m_indices)
+    h = swiglu(gu)
+    valid = np.asarray(m_indices) >= 0
+    valid &= np.asarray(m_indices) < np.asarray(w1q).shape[0]
+    h32, hq, sh = _recast_rows(h, valid, pow2)
+    y = grouped_contiguous(hq, np.nan_to_num(sh), w2q, s2, m_indices)
+    return dict(gate_up=gu, h=h, h32=h32, hq=hq, sh=sh, y=y)
+
+
+def moe_ffn_masked(xq, sx, w1q, s1, w2q, s2, masked_m, pow2: bool = False) -> dict:
+    """Expert FFN in the masked layout. xq [G,M_max,H] with sx [G,M_max,H/128]; weights as
+    in moe_ffn_contiguous; masked_m [G]. Outputs carry a leading [G, M_max]; rows
+    r >= masked_m[g] are NaN."""
+    gu = grouped_masked(xq, sx, w1q, s1, masked_m)
+    h = swiglu(gu)
+    G, M_max, I = h.shape
+    mm = np.clip(np.asarray(masked_m, np.int64), 0, M_max)
+    valid = (np.arange(M_max)[None, :] < mm[:, None]).reshape(-1)
+    h32, hq, sh = _recast_rows(h.reshape(G * M_max, I), valid, pow2)
+    hq = hq.reshape(G, M_max, I)
+    sh = sh.reshape(G, M_max, I // QBLK)
+    y = grouped_masked(hq, np.nan_to_num(sh), w2q, s2, masked_m)
+    return dict(gate_up=gu, h=h, h32=h32.reshape(G, M_max, I), hq=hq, sh=sh, y=y)
