@@ -182,6 +182,54 @@ dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, int32_t scal
                                   uint16_t* d, int32_t G, int64_t M, int64_t N, int64_t K,
                                   int64_t expected_m, void* stream);
 
+/*
+ * Gate/up GEMM of an MoE expert FFN with the SwiGLU activation and the per-token FP8
+ * re-cast fused into its epilogue (DeepGEMM article, section "swapAB and Mega MoE": the
+ * expert FFN's two GEMMs and its SwiGLU activation in one fused kernel; this is the
+ * single-GPU part, without the network transfer).
+ *   layout:    0 = dense (meta ignored, G ignored), 1 = contiguous (meta = m_indices),
+ *              2 = masked (meta = masked_m), with the row rules of the GEMMs above.
+ *   scale_fmt: DG_SCALE_F32, or DG_SCALE_UE8M0 (every sfa / sfb a power of two; the h
+ *              scales are then powers of two as well, as in the _ue8m0 casts).
+ *   a   [rows,K] e4m3 with sfa [K/128,rows] (masked: [G,M_max,K], [G,K/128,M_max]);
+ *   b   [G,2I,K] e4m3 with sfb [G,2I/128,K/128]: rows [0,I) of each group are the gate
+ *       projection, rows [I,2I) the up projection;
+ *   hq  [rows,I] e4m3 (output; masked [G,M_max,I]);
+ *   sfh [I/128,rows] fp32 (output, K-block-major like every activation scale; masked
+ *       [G,I/128,M_max]): hq and sfh are exactly the operands the down GEMM takes.
+ * With gate/up = the fp32 GEMM result of the two halves of b (computed as in the GEMMs
+ * above, without the bf16 rounding):
+ *   h = silu(gate) * up, silu(x) = x / (1 + exp(-x)), evaluated in fp32;
+ *   per row and per 128-column block of h: s = amax|h| / 448 (UE8M0: its power of two),
+ *   q = e4m3(h / s), the rule of dg_cast_fp8_per_token.
+ * Rows that are not computed (masked rows >= masked_m, contiguous blocks that start with
+ * -1) are not written. Requires I % 128 == 0, K % 128 == 0, K <= 32768, rows*K < 2^32 and
+ * 2*I*K < 2^32 (per group), M_total % 128 == 0 for the contiguous layout.
+ */
+dg_status_t dg_gemm_fp8_swiglu(int32_t layout, int32_t scale_fmt, const uint8_t* a, const float* sfa,
+                               const uint8_t* b, const float* sfb, const int32_t* meta, uint8_t* hq,
+                               float* sfh, int32_t G, int64_t M, int64_t I, int64_t K, int64_t expected_m,
+                               void* stream);
+
+/*
+ * MoE expert FFN (DeepGEMM article, section "swapAB and Mega MoE"):
+ *   y = down( SwiGLU( gate/up(x) ) ), the two grouped GEMMs with the activation and the
+ *   FP8 re-cast between them fused into the first one (dg_gemm_fp8_swiglu), then the
+ *   grouped GEMM of the same layout on (hq, sfh) with w2.
+ *   x [rows,H] e4m3 with sfx [H/128,rows] (masked: [G,M_max,H], [G,H/128,M_max]);
+ *   w1 [G,2I,H] with sfw1 [G,2I/128,H/128] (gate rows, then up rows);
+ *   w2 [G,H,I] with sfw2 [G,H/128,I/128];
+ *   hq, sfh: caller-provided workspace for the FP8 activation between the GEMMs, shaped
+ *       as the outputs of dg_gemm_fp8_swiglu (they hold it when the stream has run);
+ *   y [rows,H] bf16 (output; masked [G,M_max,H]).
+ * Both launches go to `stream` in order. Every argument of both GEMMs is validated before
+ * either is launched; the requirements are those of dg_gemm_fp8_swiglu plus H % 128 == 0.
+ */
+dg_status_t dg_moe_ffn_fp8(int32_t layout, int32_t scale_fmt, const uint8_t* x, const float* sfx,
+                           const uint8_t* w1, const float* sfw1, const uint8_t* w2, const float* sfw2,
+                           const int32_t* meta, uint8_t* hq, float* sfh, uint16_t* y, int32_t G, int64_t M,
+                           int64_t H, int64_t I, int64_t expected_m, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status_t status);
 

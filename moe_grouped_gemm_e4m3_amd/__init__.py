@@ -18,6 +18,8 @@ Entry points (same names as the C ABI, without the dg_ prefix):
   gemm_fp8_nt(a, sfa, b, sfb)                -> d [M,N] bf16
   grouped_gemm_contiguous(a, sfa, b, sfb, m_indices)      -> d [M_total,N] bf16
   grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m) -> d [G,M_max,N] bf16
+  gemm_fp8_swiglu(layout, a, sfa, w1, sfw1, meta)         -> (hq, sfh): the FP8 SwiGLU activation
+  moe_ffn_fp8(layout, x, sfx, w1, sfw1, w2, sfw2, meta)    -> (y bf16, hq, sfh): the expert FFN
 """
 from __future__ import annotations
 
@@ -66,6 +68,8 @@ def lib() -> ctypes.CDLL:
                        "dg_grouped_gemm_contiguous", "dg_grouped_gemm_masked"):
                 getattr(L, fn + sfx).restype = ctypes.c_int
         L.dg_gemm_fp8_scheduled.argtypes = [I32, I32, I32, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        L.dg_gemm_fp8_swiglu.argtypes = [I32, I32, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        L.dg_moe_ffn_fp8.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_gemm_fp8_scheduled.restype = ctypes.c_int
         L.dg_status_string.argtypes = [ctypes.c_int]
         L.dg_status_string.restype = ctypes.c_char_p
@@ -215,3 +219,78 @@ def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.
                                          expected_m, _stream(a.device))
     _check(st)
     return d
+
+
+# ---- expert FFN ------------------------------------------------------------------------
+def _ffn_shapes(layout, a, sfa, w1, meta):
+    """Checks the gate/up operands; returns (G, M, K, I) and the hq / sfh shapes."""
+    if layout == LAYOUT_MASKED:
+        G, M, K = a.shape
+        want_sfa = (G, K // 128, M)
+    else:
+        M, K = a.shape
+        G = w1.shape[0] if w1.dim() == 3 else 1
+        want_sfa = (K // 128, M)
+    two_i = w1.shape[-2]
+    I = two_i // 2
+    want_w1 = (G, two_i, K) if (layout != LAYOUT_DENSE or w1.dim() == 3) else (two_i, K)
+    if tuple(sfa.shape) != want_sfa or tuple(w1.shape) != want_w1 or two_i % 2:
+        raise ValueError("shape mismatch: a %s sfa %s w1 %s" % (tuple(a.shape), tuple(sfa.shape), tuple(w1.shape)))
+    if layout == LAYOUT_CONTIGUOUS and (meta is None or tuple(meta.shape) != (M,)):
+        raise ValueError("contiguous layout needs m_indices [M_total]")
+    if layout == LAYOUT_MASKED and (meta is None or tuple(meta.shape) != (G,)):
+        raise ValueError("masked layout needs masked_m [G]")
+    if layout == LAYOUT_MASKED:
+        return G, M, K, I, (G, M, I), (G, I // 128, M)
+    return G, M, K, I, (M, I), (I // 128, M)
+
+
+def gemm_fp8_swiglu(layout, a, sfa, w1, sfw1, meta=None, expected_m: int = 0, hq=None, sfh=None,
+                    ue8m0: bool = False):
+    """Gate/up GEMM with the SwiGLU + per-token FP8 cast epilogue. w1 [G,2I,K] (gate rows,
+    then up rows), sfw1 [G,2I/128,K/128]; returns hq (e4m3 [rows,I]) and sfh ([I/128,rows]),
+    with a leading [G] for the masked layout."""
+    _operands(a, sfa, w1, sfw1)
+    G, M, K, I, hq_shape, sh_shape = _ffn_shapes(layout, a, sfa, w1, meta)
+    if meta is not None:
+        _need(meta, torch.int32, "meta")
+    hq = torch.empty(hq_shape, dtype=torch.uint8, device=a.device) if hq is None else hq
+    sfh = torch.empty(sh_shape, dtype=torch.float32, device=a.device) if sfh is None else sfh
+    _need(hq, torch.uint8, "hq")
+    _need(sfh, torch.float32, "sfh")
+    if tuple(hq.shape) != hq_shape or tuple(sfh.shape) != sh_shape:
+        raise ValueError("hq / sfh shape mismatch")
+    st = lib().dg_gemm_fp8_swiglu(layout, SCALE_UE8M0 if ue8m0 else SCALE_F32, _ptr(a), _ptr(sfa), _ptr(w1),
+                                  _ptr(sfw1), None if meta is None else _ptr(meta), _ptr(hq), _ptr(sfh), G, M, I, K,
+                                  expected_m, _stream(a.device))
+    _check(st)
+    return hq, sfh
+
+
+def moe_ffn_fp8(layout, x, sfx, w1, sfw1, w2, sfw2, meta=None, expected_m: int = 0, hq=None, sfh=None, y=None,
+                ue8m0: bool = False):
+    """Expert FFN: y = down(SwiGLU(gate/up(x))). w2 [G,H,I], sfw2 [G,H/128,I/128]. Returns
+    (y bf16 [rows,H] (masked [G,M_max,H]), hq, sfh) - the last two are the workspace."""
+    _operands(x, sfx, w1, sfw1)
+    _need(w2, torch.uint8, "w2")
+    _need(sfw2, torch.float32, "sfw2")
+    G, M, H, I, hq_shape, sh_shape = _ffn_shapes(layout, x, sfx, w1, meta)
+    want_w2 = (G, H, I) if (layout != LAYOUT_DENSE or w2.dim() == 3) else (H, I)
+    if tuple(w2.shape) != want_w2 or tuple(sfw2.shape)[-2:] != (H // 128, I // 128):
+        raise ValueError("shape mismatch: w2 %s sfw2 %s" % (tuple(w2.shape), tuple(sfw2.shape)))
+    if meta is not None:
+        _need(meta, torch.int32, "meta")
+    hq = torch.empty(hq_shape, dtype=torch.uint8, device=x.device) if hq is None else hq
+    sfh = torch.empty(sh_shape, dtype=torch.float32, device=x.device) if sfh is None else sfh
+    y_shape = (G, M, H) if layout == LAYOUT_MASKED else (M, H)
+    y = torch.empty(y_shape, dtype=torch.bfloat16, device=x.device) if y is None else y
+    _need(hq, torch.uint8, "hq")
+    _need(sfh, torch.float32, "sfh")
+    _need(y, torch.bfloat16, "y")
+    if tuple(hq.shape) != hq_shape or tuple(sfh.shape) != sh_shape or tuple(y.shape) != y_shape:
+        raise ValueError("hq / sfh / y shape mismatch")
+    st = lib().dg_moe_ffn_fp8(layout, SCALE_UE8M0 if ue8m0 else SCALE_F32, _ptr(x), _ptr(sfx), _ptr(w1), _ptr(sfw1),
+                              _ptr(w2), _ptr(sfw2), None if meta is None else _ptr(meta), _ptr(hq), _ptr(sfh),
+                              _ptr(y), G, M, H, I, expected_m, _stream(x.device))
+    _check(st)
+    return y, hq, sfh

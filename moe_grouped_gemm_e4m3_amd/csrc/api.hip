@@ -1,6 +1,7 @@
 // api.hip - the C ABI declared in include/dg.h: argument validation (before any HIP
 // call), device check, schedule dispatch, status reporting.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -118,6 +119,52 @@ dg_status_t run_cast(bool per_block, bool pow2, const void* x, dg_input_dtype_t 
   return launched(e, name);
 }
 
+// Common part of the SwiGLU GEMM and the expert FFN: every host-side argument check of the
+// gate/up GEMM; then (unless validate_only) the device check and the launch.
+dg_status_t run_swiglu(int32_t layout, int32_t scale_fmt, const uint8_t* a, const float* sfa, const uint8_t* b,
+                       const float* sfb, const int32_t* meta, uint8_t* hq, float* sfh, int64_t G, int64_t M,
+                       int64_t I, int64_t K, int64_t expected_m, void* stream, const char* name, bool validate_only) {
+  if (layout < 0 || layout > 2) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown layout %d", name, layout);
+  if (scale_fmt != DG_SCALE_F32 && scale_fmt != DG_SCALE_UE8M0)
+    return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown scale format %d", name, scale_fmt);
+  const dg::Layout L = static_cast<dg::Layout>(layout);
+  if (L == dg::Layout::Dense) G = 1;
+  if (M < 0 || G < 0 || I < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
+  dg_status_t st = check_nk(2 * I, K);
+  if (st != DG_OK) return st;
+  if (I % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: I=%lld is not a multiple of 128", name, (long long)I);
+  if (M >= kMaxDim || G >= kMaxDim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: M or G >= 2^31", name);
+  if (L == dg::Layout::Contiguous) {
+    if (M % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: M_total=%lld is not a multiple of 128", name, (long long)M);
+    if (G < 1) return fail(DG_ERR_INVALID_ARGUMENT, "%s: G must be >= 1", name);
+  }
+  // the fused kernel addresses one group's operands with 32-bit offsets and keeps a tile's
+  // weight scales for every K block in LDS
+  if (K / kQ > 256 || M * K >= ((int64_t)1 << 32) || 2 * I * K >= ((int64_t)1 << 32) ||
+      M * (K / kQ) * 4 >= ((int64_t)1 << 32))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: needs K <= 32768, M*K < 2^32 and 2*I*K < 2^32", name);
+  if (M == 0 || I == 0 || G == 0) return ok();
+  if (!a || !sfa || !b || !sfb || !hq || !sfh || (L != dg::Layout::Dense && !meta))
+    return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(a) || !aligned16(sfa) || !aligned16(b) || !aligned16(sfb) || !aligned16(hq) || !aligned16(sfh) ||
+      (L != dg::Layout::Dense && !aligned16(meta)))
+    return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  if (validate_only) return DG_OK;
+  st = check_device();
+  if (st != DG_OK) return st;
+  dg::GemmProblem p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = nullptr;
+  p.m_indices = L == dg::Layout::Contiguous ? meta : nullptr;
+  p.masked_m = L == dg::Layout::Masked ? meta : nullptr;
+  p.M = M; p.N = 2 * I; p.K = K; p.G = (int32_t)G; p.layout = L; p.pow2 = scale_fmt == DG_SCALE_UE8M0;
+  const char* chosen = "";
+  const hipError_t e = dg::launch_gemm_swiglu(p, hq, sfh, expected_m, static_cast<hipStream_t>(stream), &chosen);
+  if (getenv("DG_LOG")) fprintf(stderr, "[dg] %s M=%lld I=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
+                                (long long)I, (long long)K, (long long)G, chosen);
+  if (e == hipErrorNotSupported) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: shape out of the kernel's range", name);
+  return launched(e, name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +238,33 @@ dg_status_t dg_gemm_fp8_scheduled(int32_t layout, int32_t schedule, int32_t scal
   const dg::Layout L = static_cast<dg::Layout>(layout);
   return run_gemm(L, schedule, scale_fmt == DG_SCALE_UE8M0, a, sfa, b, sfb, L == dg::Layout::Dense ? nullptr : meta, d,
                   L == dg::Layout::Dense ? 1 : G, M, N, K, expected_m, stream, "dg_gemm_fp8_scheduled");
+}
+
+dg_status_t dg_gemm_fp8_swiglu(int32_t layout, int32_t scale_fmt, const uint8_t* a, const float* sfa, const uint8_t* b,
+                               const float* sfb, const int32_t* meta, uint8_t* hq, float* sfh, int32_t G, int64_t M,
+                               int64_t I, int64_t K, int64_t expected_m, void* stream) {
+  return run_swiglu(layout, scale_fmt, a, sfa, b, sfb, meta, hq, sfh, G, M, I, K, expected_m, stream,
+                    "dg_gemm_fp8_swiglu", false);
+}
+
+dg_status_t dg_moe_ffn_fp8(int32_t layout, int32_t scale_fmt, const uint8_t* x, const float* sfx, const uint8_t* w1,
+                           const float* sfw1, const uint8_t* w2, const float* sfw2, const int32_t* meta, uint8_t* hq,
+                           float* sfh, uint16_t* y, int32_t G, int64_t M, int64_t H, int64_t I, int64_t expected_m,
+                           void* stream) {
+  const char* name = "dg_moe_ffn_fp8";
+  // validate both GEMMs before launching either
+  dg_status_t st = run_swiglu(layout, scale_fmt, x, sfx, w1, sfw1, meta, hq, sfh, G, M, I, H, expected_m, stream, name,
+                              true);
+  if (st != DG_OK) return st;
+  if (M == 0 || I == 0 || (layout != 0 && G == 0)) return ok();
+  if (!w2 || !sfw2 || !y) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(w2) || !aligned16(sfw2) || !aligned16(y))
+    return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  st = run_swiglu(layout, scale_fmt, x, sfx, w1, sfw1, meta, hq, sfh, G, M, I, H, expected_m, stream, name, false);
+  if (st != DG_OK) return st;
+  const dg::Layout L = static_cast<dg::Layout>(layout);
+  return run_gemm(L, 0, scale_fmt == DG_SCALE_UE8M0, hq, sfh, w2, sfw2, L == dg::Layout::Dense ? nullptr : meta, y,
+                  L == dg::Layout::Dense ? 1 : G, M, H, I, expected_m, stream, name);
 }
 
 const char* dg_status_string(dg_status_t status) {

@@ -29,15 +29,6 @@ __device__ __forceinline__ void load4(const void* base, int64_t elem, float v[4]
   }
 }
 
-// The smallest power of two >= v, and >= 2^-126, from the fp32 bits: a normal v with a
-// zero mantissa is a power of two already; otherwise the exponent goes up by one.
-__device__ __forceinline__ float pow2_ceil(float v) {
-  const uint32_t b = __float_as_uint(v);
-  if (b < 0x00800000u) return __uint_as_float(0x00800000u);  // 0, subnormal (v >= 0 here)
-  const uint32_t e = (b >> 23) + ((b & 0x007FFFFFu) ? 1u : 0u);
-  return __uint_as_float(e << 23);
-}
-
 __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
   uint32_t packed = 0;
 #pragma unroll

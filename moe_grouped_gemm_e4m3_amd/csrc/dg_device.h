@@ -36,6 +36,16 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// The smallest power of two >= v (v >= 0), and >= 2^-126, from the fp32 bits: a normal v
+// with a zero mantissa is a power of two already; otherwise the exponent goes up by one.
+// This is the UE8M0 (power-of-two) scale of the casts.
+__device__ __forceinline__ float pow2_ceil(float v) {
+  const uint32_t b = __float_as_uint(v);
+  if (b < 0x00800000u) return __uint_as_float(0x00800000u);  // 0 and subnormals
+  const uint32_t e = (b >> 23) + ((b & 0x007FFFFFu) ? 1u : 0u);
+  return __uint_as_float(e << 23);
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs here are finite or NaN).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

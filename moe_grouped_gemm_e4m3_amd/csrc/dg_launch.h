@@ -33,6 +33,13 @@ enum class Schedule : int { Auto = 0, Decode = 1, Tile128 = 2, Tile256 = 3 };
 hipError_t launch_gemm(const GemmProblem& p, Schedule s, int64_t expected_m, hipStream_t stream,
                        const char** chosen);
 
+// Gate/up GEMM with the SwiGLU + per-token FP8 cast epilogue: p.b holds 2I = p.N rows per
+// group (gate rows, then up rows); writes hq [rows, I] e4m3 and sh [I/128][rows] (per group
+// for the masked layout). hipErrorNotSupported (before any launch) when the shape is out of
+// the kernel's range.
+hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int64_t expected_m, hipStream_t stream,
+                              const char** chosen);
+
 hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, int64_t M, int64_t K, uint8_t* q,
                                  float* sf, hipStream_t stream);
 hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q, float* sf,

@@ -44,6 +44,10 @@ struct KParams {
   int tiles_m, tiles_n;
   int nwg;
   bool pow2;  // every scale is a power of two: the matrix unit applies them (where supported)
+  // SwiGLU epilogue (gate/up GEMM of an expert FFN): b holds 2I rows per group, gate rows
+  // [0, I) then up rows [I, 2I); the output is h = silu(gate) * up re-cast to FP8 per token
+  uint8_t* hq;  // [rows, I] e4m3 (masked: [G, M_max, I])
+  float* sh;    // [I/128][rows] fp32 scales (masked: [G][I/128][M_max])
 };
 
 __device__ __forceinline__ int64_t clamp_rows(int64_t v, int64_t hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
@@ -990,9 +994,108 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
 //
 // The loop issues no vector-memory loads besides the direct ones (the tile's weight scales
 // are staged in LDS up front), so the explicit vmcnt values count exactly those.
+//
+// kSwiglu: the gate/up GEMM of an expert FFN with the activation and the FP8 re-cast in
+// the epilogue (DeepGEMM article, "swapAB and Mega MoE": the FFN's two GEMMs and its
+// SwiGLU activation fused). A 256-row B tile holds 128 gate rows and the 128 matching up
+// rows, so a workgroup owns one 128-column block of h = silu(gate) * up for BM tokens:
+// exactly the 1x128 chunks the per-token cast needs. A wave's first TN/2 fragments are
+// gate columns and its last TN/2 the same columns of up, so every lane holds both
+// operands of its h elements in registers.
 constexpr int kMaxKb3 = 256;  // K blocks the direct-load tile kernel supports (K <= 32768)
 
-template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2>
+// silu(g) * u in fp32: exp and reciprocal on the transcendental unit (a few ulp each)
+__device__ __forceinline__ float swiglu1(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);  // exp(-g)
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Epilogue of the SwiGLU tile: h = silu(gate) * up from the fp32 accumulators, then the
+// per-token cast of h (DeepSeek-V3 repo review, "Innovations" item 4: one scale per 128
+// elements; "Risks" item 6: bound 448): per row of the tile's 128 h columns
+// amax -> s = amax / 448 (or its power of two) -> q = e4m3(h / s), s == 0 giving signed
+// zeros. Row maxima combine through LDS (every wave holds 32 of the 128 columns), the
+// codes are staged in LDS and leave as 16-byte row segments. The LDS ring is free here.
+template <int BM, int WM, int WN, int TM, int TN, Layout L, bool kPow2>
+__device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM][TN], uint8_t* smem, int g, int tn,
+                                                int64_t m0, int64_t valid, int act) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int HF = TN / 2;                 // h fragments (16 columns each) per wave
+  constexpr int PART = WN * 16;              // partial maxima per row: one per (wave column, lane column)
+  constexpr int PST = BM + 4;                // padded stride of a partial column (spreads LDS banks)
+  constexpr int TPR = NT / BM;               // threads reducing one row
+  static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0 && PART % TPR == 0, "row reduction split");
+  static_assert(HF * 16 * WN == (int)kQ, "a tile holds one 128-column block of h");
+  float* sAm = reinterpret_cast<float*>(smem);  // [PART][PST]
+  float* sS = sAm + PART * PST;                 // [BM] row scales
+  uint8_t* sQ = reinterpret_cast<uint8_t*>(sS + BM);  // [BM][128] codes
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w % WM, wn = w / WM;
+  const int fr = l & 15, g4 = l >> 4;
+  const int64_t I = p.N / 2;
+
+  __syncthreads();  // every wave is past its last read of the LDS ring
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (L == Layout::Masked && i >= act) continue;
+    float pm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < HF; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float h = swiglu1(acc[i][jj][r], acc[i][jj + HF][r]);
+        acc[i][jj][r] = h;
+        pm[r] = fmaxf(pm[r], fabsf(h));
+      }
+    *reinterpret_cast<float4*>(sAm + (wn * 16 + fr) * PST + (i * WM + wm) * 16 + 4 * g4) =
+        make_float4(pm[0], pm[1], pm[2], pm[3]);
+  }
+  __syncthreads();
+  {
+    const int row = t / TPR, part = t % TPR;
+    float am = 0.f;
+#pragma unroll
+    for (int k = 0; k < PART / TPR; ++k) am = fmaxf(am, sAm[(part * (PART / TPR) + k) * PST + row]);
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, TPR));
+    const float s = kPow2 ? pow2_ceil(am / 448.0f) : am / 448.0f;
+    if (part == 0) {
+      sS[row] = s;
+      if (m0 + row < valid) {
+        float* SH = p.sh + (L == Layout::Masked ? (int64_t)g * (I / kQ) * p.M : 0);
+        SH[(int64_t)tn * p.M + m0 + row] = s;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (L == Layout::Masked && i >= act) continue;
+    const int rb = (i * WM + wm) * 16 + 4 * g4;
+    const float4 s4 = *reinterpret_cast<const float4*>(sS + rb);
+    const float sr[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int jj = 0; jj < HF; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float h = acc[i][jj][r];
+        const uint32_t code = sr[r] == 0.0f ? ((__float_as_uint(h) >> 24) & 0x80u) : e4m3_encode(h / sr[r]);
+        sQ[(rb + r) * (int)kQ + wn * (HF * 16) + jj * 16 + fr] = (uint8_t)code;
+      }
+  }
+  __syncthreads();
+  uint8_t* HQ = p.hq + (L == Layout::Masked ? (int64_t)g * p.M * I : 0);
+#pragma unroll
+  for (int idx = t; idx < BM * 8; idx += NT) {
+    const int row = idx >> 3, c16 = idx & 7;
+    if (m0 + row < valid)
+      *reinterpret_cast<uint4*>(HQ + (m0 + row) * I + (int64_t)tn * kQ + c16 * 16) =
+          *reinterpret_cast<const uint4*>(sQ + row * (int)kQ + c16 * 16);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2, bool kSwiglu = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1010,6 +1113,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
   static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
   static_assert(STAGES * STAGE_BYTES + NB * kMaxKb3 * 4 <= 160 * 1024, "LDS");
+  static_assert(!kSwiglu || (BN == 2 * (int)kQ && TN % 2 == 0), "SwiGLU tile: 128 gate + 128 up rows");
+  static_assert(!kSwiglu || WN * 16 * (BM + 4) * 4 + BM * 4 + BM * (int)kQ <= STAGES * STAGE_BYTES,
+                "SwiGLU epilogue fits in the LDS ring");
+  constexpr int NH = kSwiglu ? 2 : 1;  // weight-scale blocks a wave's fragments span
+  constexpr int FPH = TN / NH;         // fragments per scale block
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) float sSB[NB][kMaxKb3];  // this tile's weight scales
 
@@ -1044,7 +1152,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   const uint8_t* A = p.a + (L == Layout::Masked ? (int64_t)g * p.M * K : 0);
   const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0);
   const uint8_t* B = p.b + (int64_t)g * p.N * K;
-  const float* SB = p.sfb + ((int64_t)g * (p.N / kQ) + n0 / kQ) * nkb;
+  const float* SB = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
+  // B row of tile row r: plain tiles take rows n0.., SwiGLU tiles the gate block tn and
+  // the up block I/128 + tn (I = N/2)
+  auto b_row = [&](int r) -> int64_t {
+    if constexpr (kSwiglu) return r < (int)kQ ? (int64_t)tn * kQ + r : p.N / 2 + (int64_t)tn * kQ + (r - (int)kQ);
+    else return n0 + r;
+  };
   uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
 
   const int t = threadIdx.x, l = t & 63;
@@ -1063,7 +1177,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 #pragma unroll
   for (int u = 0; u < BDMA; ++u) {
     const int row = (u * NW + w) * 8 + (l >> 3);
-    boff[u] = (uint32_t)((n0 + row) * K) + (uint32_t)(((l & 7) ^ ((l >> 3) & 7)) << 4);
+    boff[u] = (uint32_t)(b_row(row) * K) + (uint32_t)(((l & 7) ^ ((l >> 3) & 7)) << 4);
   }
   const uint32_t soff = (uint32_t)(clamp_rows(m0 + w * SROWS + (l < SROWS ? l : 0), valid - 1) * 4);
 
@@ -1080,7 +1194,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 
   // the tile's weight scales for every K block, through LDS: the loop below must issue no
   // vector-memory load besides the direct-to-LDS ones (its vmcnt waits count only those)
-  for (int i = t; i < NB * nkb; i += 64 * NW) sSB[i / nkb][i % nkb] = SB[(i / nkb) * nkb + i % nkb];
+  for (int i = t; i < NB * nkb; i += 64 * NW) {
+    const int bi = i / nkb, kb = i % nkb;
+    sSB[bi][kb] = SB[(b_row(bi * (int)kQ) / kQ) * nkb + kb];
+  }
   __syncthreads();
 
   v4f acc[TM][TN];
@@ -1095,16 +1212,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   // interleave by strips, so a partly valid tile (masked layout) leaves every wave a
   // similar number of active strips
   const uint32_t a_lane = (uint32_t)((wm * 16 + fr) * kQ);
-  const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * WTN + fr) * kQ);
+  // a wave's columns: WTN consecutive tile rows of B, or (SwiGLU) WTN/2 gate rows and the
+  // same WTN/2 up rows; fragment j reads tile rows frag_row(j) + wave offset + fr
+  const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * (WTN / NH) + fr) * kQ);
+  auto frag_row = [](int j) { return kSwiglu ? (j / FPH) * (int)kQ + (j % FPH) * 16 : j * 16; };
   const uint32_t s_lane = (uint32_t)((BM + BN) * kQ + (wm * 16 + 4 * g4) * 4);
-  const int wnb = (wn * WTN) / (int)kQ;  // this wave's weight-scale column block
+  const int wnb = kSwiglu ? 0 : (wn * WTN) / (int)kQ;  // weight-scale block of fragment 0
 
   auto read_b = [&](v8i (&bf)[TN], int stage) {
     const uint8_t* b_s = smem + stage * STAGE_BYTES + b_lane;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bf[j] = cat8(*reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw0),
-                   *reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw1));
+      bf[j] = cat8(*reinterpret_cast<const v4i*>(b_s + frag_row(j) * kQ + sw0),
+                   *reinterpret_cast<const v4i*>(b_s + frag_row(j) * kQ + sw1));
   };
   auto read_a = [&](v8i& af, float4& s4, int stage, int i) {
     const uint8_t* st = smem + stage * STAGE_BYTES;
@@ -1114,10 +1234,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   };
 
   v4f pp[2][TN];
-  float4 tt[2];
+  float4 tt[2][NH];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-    tt[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) tt[q][h] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < TN; ++j) pp[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -1130,9 +1251,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   }
   auto promote = [&](int slot, int strip) {
     if (L == Layout::Masked && strip >= act) return;
-    const float4 tp = tt[slot];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
+      const float4 tp = tt[slot][j / FPH];
       acc[strip][j][0] = fmaf(pp[slot][j][0], tp.x, acc[strip][j][0]);
       acc[strip][j][1] = fmaf(pp[slot][j][1], tp.y, acc[strip][j][1]);
       acc[strip][j][2] = fmaf(pp[slot][j][2], tp.z, acc[strip][j][2]);
@@ -1164,7 +1285,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   // next K block's fragments (stage `sn`) replace them, B as the last strip's MFMAs
   // consume it
   auto kblock = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, float4& s0) {
-    const float sb = sSB[wnb][kb];
+    float sb[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) sb[h] = sSB[wnb + h][kb];
     v8i af[2];
     float4 s4[2];
     af[0] = a0;
@@ -1174,7 +1297,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       const int c = i & 1;
       read_a(af[c ^ 1], s4[c ^ 1], st, i + 1);
       strip(af[c], bf, c, i, i == 0 ? TM - 1 : i - 1);  // strip 0 promotes the previous K block's last
-      tt[c] = factor(s4[c], sb);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) tt[c][h] = factor(s4[c], sb[h]);
     }
     // every read of stage st is issued; wait for the next stage, then recycle stage st
     __builtin_amdgcn_sched_barrier(0);
@@ -1195,7 +1319,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-    tt[1] = factor(s4[1], sb);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) tt[1][h] = factor(s4[1], sb[h]);
   };
 
   // power-of-two scales: the matrix unit applies them. Lane l supplies the E8M0 scale of
@@ -1210,7 +1335,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     ea = (int)(*reinterpret_cast<const uint32_t*>(st + e_lane + 64 * WM * i) >> 23);
   };
   auto kblock2 = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, int& e0) {
-    const int eb = (int)(__float_as_uint(sSB[wnb][kb]) >> 23);
+    int eb[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) eb[h] = (int)(__float_as_uint(sSB[wnb + h][kb]) >> 23);
     v8i af[2];
     int ea[2];
     af[0] = a0;
@@ -1221,7 +1348,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       read_a2(af[c ^ 1], ea[c ^ 1], st, i + 1);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        if (!(L == Layout::Masked && i >= act)) acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
+        if (!(L == Layout::Masked && i >= act))
+          acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb[j / FPH]);
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -1231,7 +1359,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       if (!(L == Layout::Masked && TM - 1 >= act))
-        acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb);
+        acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb[j / FPH]);
     read_b(bf, sn);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -1268,6 +1396,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   }
   wait_vmcnt<0>();     // drain the tail reloads before leaving
 
+  if constexpr (kSwiglu) {
+    swiglu_epilogue<BM, WM, WN, TM, TN, L, kPow2>(p, acc, smem, g, tn, m0, valid, act);
+    return;
+  }
+
   // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
@@ -1297,7 +1430,7 @@ hipError_t run_tile2(KParams kp, hipStream_t s) {
 
 // direct-to-LDS tile schedule; hipErrorNotSupported when the problem exceeds what its
 // 32-bit per-lane offsets or its LDS table of weight scales can address
-template <int BM, int BN, int WM, int WN, int STAGES, Layout L>
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kSwiglu = false>
 hipError_t run_tile3(KParams kp, hipStream_t s) {
   if (kp.N % BN != 0 || kp.nkb > kMaxKb3 || kp.M * kp.K >= ((int64_t)1 << 32) ||
       kp.N * kp.K >= ((int64_t)1 << 32) || kp.M * kp.nkb * 4 >= ((int64_t)1 << 32))
@@ -1309,9 +1442,9 @@ hipError_t run_tile3(KParams kp, hipStream_t s) {
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
   if (kp.pow2)
-    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, true><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, true, kSwiglu><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
   else
-    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, false><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
+    gemm_tile3_kernel<BM, BN, WM, WN, STAGES, L, false, kSwiglu><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
   return hipGetLastError();
 }
 
@@ -1653,6 +1786,35 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       }
       pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Contiguous>(kp, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int64_t expected_m, hipStream_t stream,
+                              const char** chosen) {
+  KParams kp{};
+  kp.a = p.a; kp.sfa = p.sfa; kp.b = p.b; kp.sfb = p.sfb; kp.d = nullptr;
+  kp.m_indices = p.m_indices; kp.masked_m = p.masked_m;
+  kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G; kp.pow2 = p.pow2;
+  kp.hq = hq; kp.sh = sh;
+  const char* force = getenv("DG_TILE");
+  auto is = [&](const char* name) { return force && strcmp(force, name) == 0; };
+  auto pick = [&](const char* name) { if (chosen) *chosen = name; };
+  switch (p.layout) {
+    case Layout::Contiguous:
+      pick("tile3_swiglu_128x256");
+      return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true>(kp, stream);
+    case Layout::Masked:
+      if (is("t3_128x256") || (!force && expected_m > 0 && expected_m <= 64)) {
+        pick("tile3_swiglu_128x256");
+        return run_tile3<128, 256, 2, 4, 3, Layout::Masked, true>(kp, stream);
+      }
+      pick("tile3_swiglu_256x256");
+      return run_tile3<256, 256, 2, 4, 2, Layout::Masked, true>(kp, stream);
+    case Layout::Dense:
+      (void)is;
+      pick("tile3_swiglu_128x256");
+      return run_tile3<128, 256, 2, 4, 3, Layout::Dense, true>(kp, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -15,7 +15,8 @@ Recipes (one generator stream per (seed, tensor id), numpy PCG64):
   * contiguous MoE layout: per-expert routed row counts ~ Multinomial(tokens, 1/G each),
     each expert's rows padded up to a multiple of 128; m_indices holds the expert id of
     each row, -1 on padding rows; padding rows of A are zero;
-  * masked MoE layout: valid rows per expert ~ uniform on {0, ..., M_max} (inclusive).
+  * masked MoE layout: valid rows per expert ~ uniform on {0, ..., M_max} (inclusive);
+  * expert FFN weights: gate/up W1 [G, 2I, H] and down W2 [G, H, I], both ~ N(0, 0.02).
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ QBLK = 128
 
 # tensor ids: one independent stream per role
 TID_A, TID_B, TID_OUTLIER, TID_ROUTE, TID_MASK = 1, 2, 3, 4, 5
+TID_W1, TID_W2 = 6, 7  # expert FFN: gate/up and down projections
 
 
 def rng(seed: int, tensor_id: int) -> np.random.Generator:
@@ -102,3 +104,10 @@ def masked_inputs(G: int, M_max: int, N: int, K: int, seed: int = 0, b_std: floa
     a = normal((G, M_max, K), seed, TID_A)
     b = normal((G, N, K), seed, TID_B, std=b_std)
     return a, b, masked_m
+
+
+def ffn_weights(G: int, H: int, I: int, seed: int = 0, std: float = 0.02):
+    """fp32 expert FFN weights: W1 [G,2I,H] (gate rows, then up rows), W2 [G,H,I]."""
+    w1 = normal((G, 2 * I, H), seed, TID_W1, std=std)
+    w2 = normal((G, H, I), seed, TID_W2, std=std)
+    return w1, w2

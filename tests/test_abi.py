@@ -107,3 +107,36 @@ def test_cast_argument_errors(L):
     b = L.dg_cast_fp8_per_block
     assert b(P, 0, 100, 512, P, P, None) == 2
     assert b(P, 1, 128, 384, P, Q, None) == 3
+
+
+def test_swiglu_and_ffn_argument_errors(L):
+    w = L.dg_gemm_fp8_swiglu
+    #        layout fmt a  sfa b  sfb meta hq sfh G  M     I    K
+    assert w(3, 0, P, P, P, P, P, P, P, 4, 1024, 256, 512, 0, None) == 1      # unknown layout
+    assert w(1, 2, P, P, P, P, P, P, P, 4, 1024, 256, 512, 0, None) == 1      # unknown scale format
+    assert w(1, 0, P, P, P, P, P, P, P, 4, 1024, 192, 512, 0, None) == 2      # I % 128
+    assert w(1, 0, P, P, P, P, P, P, P, 4, 1000, 256, 512, 0, None) == 2      # M_total % 128
+    assert w(1, 0, P, P, P, P, P, P, P, 4, 1024, 256, 500, 0, None) == 2      # K % 128
+    assert w(1, 0, P, P, P, P, P, P, P, 4, 1024, 256, 128 * 257, 0, None) == 2  # K > 32768
+    assert w(2, 0, P, P, P, P, P, P, P, 4, 1 << 20, 256, 1 << 13, 0, None) == 2  # rows*K >= 2^32
+    assert w(1, 0, P, P, P, P, None, P, P, 4, 1024, 256, 512, 0, None) == 1   # m_indices null
+    assert w(2, 0, P, P, P, P, P, None, P, 4, 64, 256, 512, 0, None) == 1     # hq null
+    assert w(2, 0, P, P, P, P, P, P, Q, 4, 64, 256, 512, 0, None) == 3        # sfh misaligned
+    assert w(0, 0, P, P, P, P, None, P, P, 0, 64, 256, 512, 0, None) in (0, 4)  # dense ignores meta and G
+    assert w(2, 0, P, P, P, P, P, P, P, 0, 64, 256, 512, 0, None) == 0        # G = 0: empty
+    assert w(1, 0, P, P, P, P, P, P, P, 4, 0, 256, 512, 0, None) == 0         # M = 0: empty
+    f = L.dg_moe_ffn_fp8
+    #        layout fmt x  sfx w1 s1 w2 s2 meta hq sfh y  G  M     H    I
+    assert f(1, 0, P, P, P, P, P, P, P, P, P, P, 4, 1024, 384, 256, 0, None) in (0, 4)
+    assert f(1, 0, P, P, P, P, P, P, P, P, P, P, 4, 1024, 300, 256, 0, None) == 2  # H % 128
+    assert f(1, 0, P, P, P, P, None, P, P, P, P, P, 4, 1024, 384, 256, 0, None) == 1  # w2 null
+    assert f(1, 0, P, P, P, P, P, P, P, P, P, Q, 4, 1024, 384, 256, 0, None) == 3     # y misaligned
+    assert f(2, 1, P, P, P, P, P, P, P, P, P, P, 0, 64, 384, 256, 0, None) == 0       # empty
+
+
+def test_swiglu_without_gpu_reports_device(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert L.dg_gemm_fp8_swiglu(1, 0, P, P, P, P, P, P, P, 4, 1024, 256, 512, 0, None) == 4
+    assert L.dg_moe_ffn_fp8(2, 0, P, P, P, P, P, P, P, P, P, P, 4, 64, 384, 256, 16, None) == 4

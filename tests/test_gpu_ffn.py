@@ -1,0 +1,269 @@
+"""GPU parity of the fused gate/up GEMM + SwiGLU + per-token FP8 re-cast, and of the MoE
+expert FFN (dg_gemm_fp8_swiglu, dg_moe_ffn_fp8) against the oracle's composition.
+
+Inputs are quantised by both sides (casts asserted bit-exact), so both run on the same
+bytes. The re-cast codes are checked as valid roundings of the oracle's h within the
+error band of the fp32 accumulators (tests/ffn_checks.py), the output against the GEMM
+bound plus what those choices can change."""
+import numpy as np
+import pytest
+import torch
+
+import ffn_checks as fc
+import oracle
+import synth
+from helpers import (assert_same_bits, assert_same_bytes, bf16_values, gpu_cast_blocks, gpu_cast_tokens, kmajor,
+                     say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+CONTIG, MASKED, DENSE = 1, 2, 0
+SENTINEL_Q = 0x7F  # e4m3 NaN: never produced from finite data
+
+
+@pytest.fixture(scope="module")
+def dg():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import moe_grouped_gemm_e4m3_amd as m
+    m.lib()
+    return m
+
+
+def _cast_weights(dg, w, pow2):
+    """[G,N,K] fp32 -> device (q, s) and oracle (q, s); asserted equal."""
+    G, N, K = w.shape
+    q_d, s_d = gpu_cast_blocks(dg, w.reshape(G * N, K), pow2)
+    q, s = oracle.cast_per_block(w, pow2)
+    assert_same_bytes(q_d, q.reshape(G * N, K), "weights %s" % (w.shape,))
+    assert_same_bits(s_d, s.reshape(G * N // 128, K // 128), "weight scales")
+    return (q_d.view(G, N, K), s_d.view(G, N // 128, K // 128)), (q, s)
+
+
+def _cast_tokens(dg, x, pow2):
+    """[R,K] or [G,M,K] fp32 -> device (q, s K-block-major) and oracle (q, s row-major)."""
+    q_d, s_d = gpu_cast_tokens(dg, x, pow2)
+    shp = x.shape
+    q, s = oracle.cast_per_token(x.reshape(-1, shp[-1]), pow2)
+    q = q.reshape(shp)
+    s = s.reshape(*shp[:-1], shp[-1] // 128)
+    assert_same_bytes(q_d, q, "activations")
+    assert_same_bits(s_d, kmajor(s), "activation scales")
+    return (q_d, s_d), (q, s)
+
+
+def _contiguous_case(dg, G, tokens, H, I, seed, pow2):
+    mi, _ = synth.contiguous_layout(G, tokens, seed)
+    x = synth.normal((mi.size, H), seed, synth.TID_A)
+    x[mi < 0] = 0.0
+    w1, w2 = synth.ffn_weights(G, H, I, seed)
+    (xq_d, sx_d), (xq, sx) = _cast_tokens(dg, x, pow2)
+    (w1_d, s1_d), (w1q, s1) = _cast_weights(dg, w1, pow2)
+    (w2_d, s2_d), (w2q, s2) = _cast_weights(dg, w2, pow2)
+    dev = (xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, to_dev(mi))
+    ref = oracle.moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, mi, pow2)
+    return dev, (xq, sx, w1q, s1, w2q, s2, mi), ref
+
+
+def _masked_case(dg, G, M_max, H, I, seed, pow2, masked_m=None):
+    mm = synth.masked_layout(G, M_max, seed) if masked_m is None else np.asarray(masked_m, np.int32)
+    x = synth.normal((G, M_max, H), seed, synth.TID_A)
+    w1, w2 = synth.ffn_weights(G, H, I, seed)
+    (xq_d, sx_d), (xq, sx) = _cast_tokens(dg, x, pow2)
+    (w1_d, s1_d), (w1q, s1) = _cast_weights(dg, w1, pow2)
+    (w2_d, s2_d), (w2q, s2) = _cast_weights(dg, w2, pow2)
+    dev = (xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, to_dev(mm))
+    ref = oracle.moe_ffn_masked(xq, sx, w1q, s1, w2q, s2, mm, pow2)
+    return dev, (xq, sx, w1q, s1, w2q, s2, mm), ref
+
+
+def _check_rows(rows_by_expert, xq, sx, w1q, s1, w2q, s2, ref_rows, hq_gpu, sh_gpu, y_gpu, pow2, what):
+    """Checks the re-cast and (if y_gpu is given) the output for the listed rows.
+    rows_by_expert: {expert: row indices into the flattened row arrays}."""
+    H = xq.shape[-1]
+    nkb = H // 128
+    for e, rows in rows_by_expert.items():
+        if len(rows) == 0:
+            continue
+        a_deq = fc.dequant_rows(xq[rows], sx[rows])
+        L = fc.abs_products(a_deq, fc.dequant_blocks(w1q[e], s1[e]))
+        gu = ref_rows["gate_up"][rows]
+        e_h = fc.h_band(gu, L, nkb)
+        c_lo, c_hi, s_lo, s_hi = fc.check_recast(ref_rows["h"][rows], e_h, hq_gpu[rows], sh_gpu[rows],
+                                                 ref_rows["hq"][rows], pow2, "%s expert %d" % (what, e))
+        if y_gpu is not None:
+            allow = fc.output_allowance(c_lo, c_hi, s_lo, s_hi, ref_rows["hq"][rows], ref_rows["sh"][rows],
+                                        fc.dequant_blocks(w2q[e], s2[e]))
+            fc.check_output(y_gpu[rows], ref_rows["y"][rows], allow, "%s expert %d" % (what, e))
+
+
+def _flat(ref):
+    return {k: v.reshape(-1, v.shape[-1]) for k, v in ref.items()}
+
+
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("G,tokens,H,I", [(4, 300, 512, 256), (3, 130, 384, 384), (2, 1, 128, 128)])
+def test_swiglu_contiguous(dg, G, tokens, H, I, pow2):
+    say("swiglu contiguous G=%d tokens=%d H=%d I=%d ue8m0=%d" % (G, tokens, H, I, pow2))
+    dev, (xq, sx, w1q, s1, w2q, s2, mi), ref = _contiguous_case(dg, G, tokens, H, I, 40 + G, pow2)
+    xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mi_d = dev
+    hq_d, sh_d = dg.gemm_fp8_swiglu(CONTIG, xq_d, sx_d, w1_d, s1_d, mi_d, ue8m0=pow2)
+    torch.cuda.synchronize()
+    hq = hq_d.cpu().numpy()
+    sh = kmajor(sh_d.cpu().numpy())  # [I/128, M] -> [M, I/128]
+    rows = {e: np.nonzero(mi == e)[0] for e in range(G)}
+    _check_rows(rows, xq, sx, w1q, s1, w2q, s2, ref, hq, sh, None, pow2, "swiglu contiguous")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_ffn_contiguous(dg, pow2):
+    G, tokens, H, I = 4, 400, 384, 512
+    say("ffn contiguous G=%d tokens=%d H=%d I=%d ue8m0=%d" % (G, tokens, H, I, pow2))
+    dev, (xq, sx, w1q, s1, w2q, s2, mi), ref = _contiguous_case(dg, G, tokens, H, I, 50, pow2)
+    xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mi_d = dev
+    y_d, hq_d, sh_d = dg.moe_ffn_fp8(CONTIG, xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mi_d, ue8m0=pow2)
+    torch.cuda.synchronize()
+    rows = {e: np.nonzero(mi == e)[0] for e in range(G)}
+    _check_rows(rows, xq, sx, w1q, s1, w2q, s2, ref, hq_d.cpu().numpy(), kmajor(sh_d.cpu().numpy()),
+                bf16_values(y_d), pow2, "ffn contiguous")
+    # the FFN is exactly the fused GEMM followed by the grouped GEMM on its output
+    hq2, sh2 = dg.gemm_fp8_swiglu(CONTIG, xq_d, sx_d, w1_d, s1_d, mi_d, ue8m0=pow2)
+    y2 = dg.grouped_gemm_contiguous(hq2, sh2, w2_d, s2_d, mi_d, ue8m0=pow2)
+    torch.cuda.synchronize()
+    assert torch.equal(hq2, hq_d) and torch.equal(sh2, sh_d)
+    assert torch.equal(y2.view(torch.int16), y_d.view(torch.int16))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("expected_m", [0, 32])
+def test_ffn_masked(dg, pow2, expected_m):
+    # expected_m selects the 256-row (0) or 128-row (32) SwiGLU tile and the down schedule
+    G, M_max, H, I = 4, 200, 384, 384
+    say("ffn masked G=%d M_max=%d H=%d I=%d ue8m0=%d expected_m=%d" % (G, M_max, H, I, pow2, expected_m))
+    mm = np.array([0, 200, 77, 129], np.int32)
+    dev, (xq, sx, w1q, s1, w2q, s2, _), ref = _masked_case(dg, G, M_max, H, I, 60, pow2, mm)
+    xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d = dev
+    hq_d = torch.full((G, M_max, I), SENTINEL_Q, dtype=torch.uint8, device="cuda")
+    sh_d = torch.full((G, I // 128, M_max), float("nan"), dtype=torch.float32, device="cuda")
+    y_d = torch.full((G, M_max, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dg.moe_ffn_fp8(MASKED, xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d, expected_m=expected_m, hq=hq_d, sfh=sh_d,
+                   y=y_d, ue8m0=pow2)
+    torch.cuda.synchronize()
+    hq = hq_d.cpu().numpy()
+    sh = kmajor(sh_d.cpu().numpy())  # [G, M_max, I/128]
+    yb = y_d.view(torch.int16).cpu().numpy()
+    for g in range(G):
+        assert np.all(hq[g, mm[g]:] == SENTINEL_Q), "hq rows beyond masked_m written (group %d)" % g
+        assert np.all(np.isnan(sh[g, mm[g]:])), "h scales beyond masked_m written (group %d)" % g
+        assert np.all(yb[g, mm[g]:] == -1), "y rows beyond masked_m written (group %d)" % g
+    rows = {g: g * M_max + np.arange(mm[g]) for g in range(G)}
+    _check_rows(rows, xq.reshape(-1, H), sx.reshape(-1, H // 128), w1q, s1, w2q, s2, _flat(ref),
+                hq.reshape(-1, I), sh.reshape(-1, I // 128), bf16_values(y_d).reshape(-1, H), pow2, "ffn masked")
+
+
+def test_swiglu_dense(dg):
+    M, H, I = 200, 256, 256
+    say("swiglu dense M=%d H=%d I=%d" % (M, H, I))
+    x = synth.normal((M, H), 70, synth.TID_A)
+    w1, w2 = synth.ffn_weights(1, H, I, 70)
+    (xq_d, sx_d), (xq, sx) = _cast_tokens(dg, x, False)
+    (w1_d, s1_d), (w1q, s1) = _cast_weights(dg, w1, False)
+    (w2_d, s2_d), (w2q, s2) = _cast_weights(dg, w2, False)
+    mi = np.zeros(M, np.int32)
+    ref = oracle.moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, mi)
+    y_d, hq_d, sh_d = dg.moe_ffn_fp8(DENSE, xq_d, sx_d, w1_d[0], s1_d[0], w2_d[0], s2_d[0])
+    torch.cuda.synchronize()
+    _check_rows({0: np.arange(M)}, xq, sx, w1q, s1, w2q, s2, ref, hq_d.cpu().numpy(), kmajor(sh_d.cpu().numpy()),
+                bf16_values(y_d), False, "ffn dense")
+
+
+def test_ffn_masked_all_empty(dg):
+    G, M_max, H, I = 3, 64, 128, 128
+    say("ffn masked all groups empty")
+    dev, _, _ = _masked_case(dg, G, M_max, H, I, 80, False, [0, 0, 0])
+    xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d = dev
+    hq_d = torch.full((G, M_max, I), SENTINEL_Q, dtype=torch.uint8, device="cuda")
+    y_d = torch.full((G, M_max, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    dg.moe_ffn_fp8(MASKED, xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d, hq=hq_d, y=y_d)
+    torch.cuda.synchronize()
+    assert torch.all(hq_d == SENTINEL_Q) and torch.all(y_d.view(torch.int16) == -1)
+
+
+def _exact_codes(rng, shape, exp_field):
+    """e4m3 codes with a fixed exponent field: values +-2^(e-7) * (1 + m/8)."""
+    sign = rng.integers(0, 2, size=shape).astype(np.uint8) << 7
+    mant = rng.integers(0, 8, size=shape).astype(np.uint8)
+    return sign | np.uint8(exp_field << 3) | mant
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_swiglu_epilogue_on_exact_accumulators(dg, pow2):
+    # codes and power-of-two scales chosen so that every block sum and every promoted
+    # partial is exact in fp32: the kernel's gate/up equal the oracle's, and the only
+    # freedom left is the fp32 evaluation of silu (band (|g| + 16) 2^-22 |h|)
+    G, H, I = 2, 512, 256
+    rng = np.random.default_rng(91)
+    mi = np.repeat(np.arange(G, dtype=np.int32), 128)
+    M = mi.size
+    xq = _exact_codes(rng, (M, H), 7)                     # |x| in [1, 2)
+    w1q = _exact_codes(rng, (G, 2 * I, H), 4)             # |w| in [1/8, 1/4)
+    sx = np.ldexp(1.0, rng.integers(-2, 1, size=(M, H // 128))).astype(np.float32)
+    s1 = np.ldexp(1.0, rng.integers(-1, 1, size=(G, 2 * I // 128, H // 128))).astype(np.float32)
+    w2q = _exact_codes(rng, (G, H, I), 4)
+    s2 = np.ones((G, H // 128, I // 128), np.float32)
+    ref = oracle.moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, mi, pow2)
+    say("swiglu exact accumulators ue8m0=%d" % pow2)
+    hq_d, sh_d = dg.gemm_fp8_swiglu(CONTIG, to_dev(xq), to_dev(kmajor(sx)), to_dev(w1q), to_dev(s1), to_dev(mi),
+                                    ue8m0=pow2)
+    torch.cuda.synchronize()
+    gu = ref["gate_up"]
+    g = gu[:, :I]
+    e_h = (np.abs(g) + 16.0) * 2.0 ** -22 * np.abs(ref["h"])
+    fc.check_recast(ref["h"], e_h, hq_d.cpu().numpy(), kmajor(sh_d.cpu().numpy()), ref["hq"], pow2,
+                    "exact accumulators", min_exact=0.9999)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layout", ["contiguous", "masked"])
+def test_ffn_full_size_sampled(dg, layout):
+    # the bench's FFN shapes: hidden 7168, expert intermediate 2048; the oracle checks a
+    # sample of rows of every expert
+    H, I = 7168, 2048
+    rng = np.random.default_rng(7)
+    if layout == "contiguous":
+        G, tokens = 8, 8192
+        mi, _ = synth.contiguous_layout(G, tokens, 1)
+        x = synth.normal((mi.size, H), 1, synth.TID_A)
+        x[mi < 0] = 0.0
+        rows_all = {e: np.nonzero(mi == e)[0] for e in range(G)}
+    else:
+        G, M_max = 32, 256
+        mm = synth.masked_layout(G, M_max, 1)
+        x = synth.normal((G, M_max, H), 1, synth.TID_A)
+        rows_all = {g: g * M_max + np.arange(mm[g]) for g in range(G)}
+    say("ffn full size %s" % layout)
+    w1, w2 = synth.ffn_weights(G, H, I, 1)
+    (xq_d, sx_d), (xq, sx) = _cast_tokens(dg, x, False)
+    (w1_d, s1_d), (w1q, s1) = _cast_weights(dg, w1, False)
+    (w2_d, s2_d), (w2q, s2) = _cast_weights(dg, w2, False)
+    del w1, w2
+    meta = to_dev(mi if layout == "contiguous" else mm)
+    lay = CONTIG if layout == "contiguous" else MASKED
+    y_d, hq_d, sh_d = dg.moe_ffn_fp8(lay, xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, meta,
+                                     expected_m=0 if layout == "contiguous" else int(mm.mean()))
+    torch.cuda.synchronize()
+    I_blocks = I // 128
+    xf, sxf = xq.reshape(-1, H), sx.reshape(-1, H // 128)
+    hq = hq_d.cpu().numpy().reshape(-1, I)
+    sh = kmajor(sh_d.cpu().numpy()).reshape(-1, I_blocks)
+    y = bf16_values(y_d).reshape(-1, H)
+    per = 8 if layout == "contiguous" else 2
+    for e, rows in rows_all.items():
+        if len(rows) == 0:
+            continue
+        pick = np.sort(rng.choice(rows, size=min(per, len(rows)), replace=False))
+        sub = oracle.moe_ffn_contiguous(xf[pick], sxf[pick], w1q[e:e + 1], s1[e:e + 1], w2q[e:e + 1], s2[e:e + 1],
+                                        np.zeros(len(pick), np.int32))
+        local = {0: np.arange(len(pick))}
+        _check_rows(local, xf[pick], sxf[pick], w1q[e:e + 1], s1[e:e + 1], w2q[e:e + 1], s2[e:e + 1], sub,
+                    hq[pick], sh[pick], y[pick], False, "ffn full %s expert %d" % (layout, e))
