@@ -51,11 +51,39 @@ WORKLOADS = {
                "layers": [("masked", dict(G=32, M_max=256, N=4096, K=7168)),
                           ("masked", dict(G=32, M_max=256, N=7168, K=2048))]},
     "tiny": {"desc": "dense M=128 N=256 K=512", "layers": [("dense", dict(M=128, N=256, K=512))]},
+    # expert FFN: gate/up GEMM (N = 2I) with the SwiGLU + FP8 re-cast epilogue, then the
+    # down GEMM (N = H, K = I); the same shapes as the contiguous / masked pairs above
+    "ffn_contiguous": {"desc": "MoE expert FFN, contiguous G=8, 8192 routed rows padded to 128: H=7168, I=2048",
+                       "layers": [("ffn_contiguous", dict(G=8, tokens=8192, H=7168, I=2048))]},
+    "ffn_masked": {"desc": "MoE expert FFN, masked G=32, M_max=256, valid ~U{0..256}: H=7168, I=2048",
+                   "layers": [("ffn_masked", dict(G=32, M_max=256, H=7168, I=2048))]},
 }
+FFN_KINDS = ("ffn_contiguous", "ffn_masked")
+FFN_WORKLOADS = ("ffn_contiguous", "ffn_masked")
+
+
+def weight_elems(kind, s):
+    if kind in FFN_KINDS:
+        return s["G"] * 3 * s["I"] * s["H"]
+    return s.get("G", 1) * s["N"] * s["K"]
+
+
+def swiglu_work(s, valid_rows):
+    """Flops and HBM bytes of the fused gate/up launch: A, W1 and their scales in; the FP8
+    activation h and its per-token scales out."""
+    G, H, I = s["G"], s["H"], s["I"]
+    flops = 2.0 * valid_rows * 2 * I * H
+    byts = (valid_rows * H + G * 2 * I * H + 4 * valid_rows * H // 128 + 4 * G * (2 * I // 128) * (H // 128)
+            + valid_rows * I + 4 * valid_rows * I // 128)
+    return flops, float(byts)
 
 
 def layer_work(kind, s, valid_rows):
     """Algorithmic flops and HBM bytes of one GEMM launch (valid rows only)."""
+    if kind in FFN_KINDS:  # the whole FFN: fused gate/up + down
+        f1, b1 = swiglu_work(s, valid_rows)
+        f2, b2 = layer_work(kind[4:], dict(G=s["G"], N=s["H"], K=s["I"]), valid_rows)
+        return f1 + f2, b1 + b2
     N, K = s["N"], s["K"]
     G = s.get("G", 1)
     flops = 2.0 * valid_rows * N * K
@@ -78,9 +106,14 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 * seed + 17)
-    N, K = s["N"], s["K"]
+    ffn = kind in FFN_KINDS
+    base = kind[4:] if ffn else kind
+    if ffn:
+        N, K = 2 * s["I"], s["H"]
+    else:
+        N, K = s["N"], s["K"]
     meta = None
-    if kind == "dense":
+    if base == "dense":
         rows = s["M"]
         valid = rows
         a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
@@ -88,7 +121,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
             hit = torch.rand((rows, K), generator=gen, device=dev) < 0.01
             a = torch.where(hit, a * 50.0, a)
         G = 1
-    elif kind == "contiguous":
+    elif base == "contiguous":
         mi, counts = synth.contiguous_layout(s["G"], s["tokens"], seed)
         rows = mi.size
         valid = int(counts.sum())
@@ -111,25 +144,49 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
         del w
         if kind == "dense":
             ws.append((qb, sb))
+        elif ffn:  # (gate/up, down) of every expert
+            H, I = s["H"], s["I"]
+            w = torch.randn((G * H, I), generator=gen, device=dev, dtype=torch.float32) * 0.02
+            q2, s2 = dg.cast_fp8_per_block(w, ue8m0=ue8m0)
+            del w
+            ws.append((qb.view(G, N, K), sb.view(G, N // 128, K // 128), q2.view(G, H, I),
+                       s2.view(G, H // 128, I // 128)))
         else:
             ws.append((qb.view(G, N, K), sb.view(G, N // 128, K // 128)))
     # activation scales are K-block-major: [K/128, rows], per group for the masked layout
     qa = torch.empty(tuple(a.shape), dtype=torch.uint8, device=dev)
     sa = torch.empty(tuple(a.shape[:-2]) + (K // 128, a.shape[-2]), dtype=torch.float32, device=dev)
-    if kind == "masked":
+    if base == "masked":
         d = torch.empty((s["G"], s["M_max"], N), dtype=torch.bfloat16, device=dev)
     else:
         d = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
-    return dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G, ue8m0=ue8m0)
+    L = dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G, ue8m0=ue8m0)
+    if ffn:  # the FP8 activation between the GEMMs and the FFN output
+        H, I = s["H"], s["I"]
+        lead = (s["G"], s["M_max"]) if base == "masked" else (rows,)
+        L["hq"] = torch.empty(lead + (I,), dtype=torch.uint8, device=dev)
+        L["sh"] = torch.empty(((s["G"], I // 128, s["M_max"]) if base == "masked" else (I // 128, rows)),
+                              dtype=torch.float32, device=dev)
+        L["y"] = torch.empty(lead + (H,), dtype=torch.bfloat16, device=dev)
+        L["layout"] = dg.LAYOUT_MASKED if base == "masked" else dg.LAYOUT_CONTIGUOUS
+    return L
+
+
+def expected_m(L):
+    return max(1, L["valid"] // L["G"])
 
 
 def run_layer(dg, L, copy_idx):
     """Cast the layer's activations, then its GEMM with weight copy `copy_idx`."""
-    kind, s = L["kind"], L["s"]
-    K = s["K"]
-    qb, sb = L["ws"][copy_idx % len(L["ws"])]
+    kind = L["kind"]
     u = L["ue8m0"]
     dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=u)
+    if kind in FFN_KINDS:
+        w1, s1, w2, s2 = L["ws"][copy_idx % len(L["ws"])]
+        dg.moe_ffn_fp8(L["layout"], L["qa"], L["sa"], w1, s1, w2, s2, L["meta"], expected_m=expected_m(L),
+                       hq=L["hq"], sfh=L["sh"], y=L["y"], ue8m0=u)
+        return
+    qb, sb = L["ws"][copy_idx % len(L["ws"])][:2]
     if kind == "dense":
         dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"], ue8m0=u)
     elif kind == "contiguous":
@@ -163,6 +220,30 @@ def cpu_baseline(workload, budget_s, ue8m0=False):
     import synth
     sample_desc = []
     jobs = []
+    if workload in FFN_WORKLOADS:
+        # one expert's FFN over 64 tokens: cast, gate/up GEMM, SwiGLU, re-cast, down GEMM
+        _, s = WORKLOADS[workload]["layers"][0]
+        H, I, rows = s["H"], s["I"], 64
+        x = synth.normal((rows, H), 0, synth.TID_A)
+        w1, w2 = synth.ffn_weights(1, H, I, 0)
+        w1q, s1 = oracle.cast_per_block(w1, pow2=ue8m0)
+        w2q, s2 = oracle.cast_per_block(w2, pow2=ue8m0)
+        del w1, w2
+        mi = np.zeros(rows, np.int32)
+        flops = 0.0
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            xq, sx = oracle.cast_per_token(x, pow2=ue8m0)
+            oracle.moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, mi, ue8m0)
+            flops += 2.0 * rows * 3 * I * H
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": "one expert's FFN (cast, gate/up GEMM, SwiGLU, re-cast, down GEMM) over %d tokens, "
+                          "H=%d I=%d, %d repetitions in %.1f s" % (rows, H, I, reps, dt)}
     for li, (kind, s) in enumerate(WORKLOADS[workload]["layers"]):
         N, K = s["N"], s["K"]
         rows = {"dense": s.get("M", 64), "contiguous": 64, "masked": 64}[kind]
@@ -251,7 +332,7 @@ def main():
 
     wl = WORKLOADS[args.workload]
     # weight copies so each step streams its weights from HBM, not the 256 MiB cache
-    wbytes = sum(s.get("G", 1) * s["N"] * s["K"] for _, s in wl["layers"])
+    wbytes = sum(weight_elems(kind, s) for kind, s in wl["layers"])
     copies = int(min(64, max(1, math.ceil(args.cache_bytes / wbytes))))
     layers = [build_layer(dg, torch, kind, s, args.seed + i, copies, args.ue8m0)
               for i, (kind, s) in enumerate(wl["layers"])]
@@ -286,41 +367,60 @@ def main():
     for L in layers:
         f, _ = layer_work(L["kind"], L["s"], L["valid"])
         step_flops += f
+    def grouped(L, base, a, sa, qb, sb, d):
+        u = L["ue8m0"]
+        if base == "dense":
+            dg.gemm_fp8_nt(a, sa, qb, sb, d=d, ue8m0=u)
+        elif base == "contiguous":
+            dg.grouped_gemm_contiguous(a, sa, qb, sb, L["meta"], d=d, ue8m0=u)
+        else:
+            dg.grouped_gemm_masked(a, sa, qb, sb, L["meta"], expected_m=expected_m(L), d=d, ue8m0=u)
+
     for L in layers:
         s_ = L["s"]
-        N, K = s_["N"], s_["K"]
+        kind = L["kind"]
+        ffn = kind in FFN_KINDS
+        base = kind[4:] if ffn else kind
+        K = s_["H"] if ffn else s_["K"]
 
         def cast_only(L=L):
             dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
 
-        def gemm_only(c, L=L):
-            qb, sb = L["ws"][c % len(L["ws"])]
-            u = L["ue8m0"]
-            if L["kind"] == "dense":
-                dg.gemm_fp8_nt(L["qa"], L["sa"], qb, sb, d=L["d"], ue8m0=u)
-            elif L["kind"] == "contiguous":
-                dg.grouped_gemm_contiguous(L["qa"], L["sa"], qb, sb, L["meta"], d=L["d"], ue8m0=u)
-            else:
-                dg.grouped_gemm_masked(L["qa"], L["sa"], qb, sb, L["meta"],
-                                       expected_m=max(1, L["valid"] // L["G"]), d=L["d"], ue8m0=u)
-
-        g_cast = capture(torch, lambda: [cast_only() for _ in range(copies)])
-        g_gemm = capture(torch, lambda: [gemm_only(c) for c in range(copies)])
-        for lab, gr in (("cast", g_cast), ("gemm", g_gemm)):
+        # (label, launch(c), flops and bytes of one launch, part of the step)
+        timed = [("cast", lambda c, L=L: cast_only(L), (0.0, cast_bytes(L["rows"], K)), True)]
+        if ffn:
+            H, I = s_["H"], s_["I"]
+            timed += [
+                ("swiglu gate/up N=%d K=%d" % (2 * I, H),
+                 lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
+                                                   L["meta"], expected_m=expected_m(L), hq=L["hq"], sfh=L["sh"],
+                                                   ue8m0=L["ue8m0"]),
+                 swiglu_work(s_, L["valid"]), True),
+                ("down N=%d K=%d" % (H, I),
+                 lambda c, L=L, base=base: grouped(L, base, L["hq"], L["sh"], *L["ws"][c % len(L["ws"])][2:], L["y"]),
+                 layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"]), True),
+                # the same gate/up product as a plain GEMM with bf16 output: the cost of the epilogue
+                ("plain gate/up (bf16 out, not in the step) N=%d K=%d" % (2 * I, H),
+                 lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2], L["d"]),
+                 layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"]), False),
+            ]
+        else:
+            timed.append(("gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
+                                                                   *L["ws"][c % len(L["ws"])][:2], L["d"]),
+                          layer_work(kind, s_, L["valid"]), True))
+        for lab, fn, (f, b), in_step in timed:
+            gr = capture(torch, lambda fn=fn: [fn(c) for c in range(copies)])
             n = max(1, reps // copies)
             time_graphs(torch, [gr], 2)
             ms = time_graphs(torch, [gr], n)
             avg_us = ms / (n * copies) * 1e3
-            if lab == "gemm":
-                f, b = layer_work(L["kind"], s_, L["valid"])
-                bound = "hbm" if f / b < RIDGE else "mfma"
-            else:
-                f, b = 0.0, cast_bytes(L["rows"], K)
-                bound = "hbm"
-            kernels.append({"kernel": lab, "layer": "%s N=%d K=%d" % (L["kind"], N, K), "avg_us": avg_us,
+            bound = "hbm" if (f == 0.0 or f / b < RIDGE) else "mfma"
+            layer = kind if ffn else "%s N=%d K=%d" % (kind, s_["N"], K)
+            kernels.append({"kernel": lab, "layer": layer, "avg_us": avg_us,
                             "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
-                            "bound": bound, "flops": f, "bytes": b, "launches": n * copies})
-    dom = max(kernels, key=lambda k: k["avg_us"])
+                            "bound": bound, "flops": f, "bytes": b, "launches": n * copies, "in_step": in_step})
+            del gr
+    dom = max((k for k in kernels if k["in_step"]), key=lambda k: k["avg_us"])
     if dom["bound"] == "hbm":
         achieved, peak, unit = dom["gbs"], PEAK_HBM_GBS, "GB/s"
     else:
@@ -334,8 +434,11 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
         "config": {"workload": wl["desc"], "weight_copies": copies,
                    "scales": "UE8M0 (powers of two)" if args.ue8m0 else "fp32 (amax / 448)",
-                   "step": "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM (bf16 out), "
-                           "per layer; replayed from HIP graphs"},
+                   "step": ("per-token FP8 cast of fp32 activations + expert FFN: gate/up GEMM with fused "
+                            "SwiGLU and FP8 re-cast, then the down GEMM (bf16 out); replayed from HIP graphs"
+                            if args.workload in FFN_WORKLOADS else
+                            "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM (bf16 out), "
+                            "per layer; replayed from HIP graphs")},
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5),
         "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

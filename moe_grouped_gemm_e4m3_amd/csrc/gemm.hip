@@ -999,9 +999,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile2_kernel(KParams p) {
 // the epilogue (DeepGEMM article, "swapAB and Mega MoE": the FFN's two GEMMs and its
 // SwiGLU activation fused). A 256-row B tile holds 128 gate rows and the 128 matching up
 // rows, so a workgroup owns one 128-column block of h = silu(gate) * up for BM tokens:
-// exactly the 1x128 chunks the per-token cast needs. A wave's first TN/2 fragments are
-// gate columns and its last TN/2 the same columns of up, so every lane holds both
-// operands of its h elements in registers.
+// exactly the 1x128 chunks the per-token cast needs.
 constexpr int kMaxKb3 = 256;  // K blocks the direct-load tile kernel supports (K <= 32768)
 
 // silu(g) * u in fp32: exp and reciprocal on the transcendental unit (a few ulp each)
@@ -1014,42 +1012,139 @@ __device__ __forceinline__ float swiglu1(float g, float u) {
 // per-token cast of h (DeepSeek-V3 repo review, "Innovations" item 4: one scale per 128
 // elements; "Risks" item 6: bound 448): per row of the tile's 128 h columns
 // amax -> s = amax / 448 (or its power of two) -> q = e4m3(h / s), s == 0 giving signed
-// zeros. Row maxima combine through LDS (every wave holds 32 of the 128 columns), the
-// codes are staged in LDS and leave as 16-byte row segments. The LDS ring is free here.
+// zeros. Waves wn = 0, 1 hold gate columns, wn = 2, 3 the same columns of up (so the main
+// loop is the plain one: one weight-scale block per wave). Partner waves wn and wn ^ 2 swap
+// half of their strips through LDS: the gate wave forms h for the first TM/2 strips, the up
+// wave for the last TM/2. Row maxima combine through LDS, the codes are staged in LDS and
+// leave as 16-byte row segments. The LDS ring is free here.
+//
+// Both sides run the same code; a side's choices are selects of values read with
+// compile-time indices (indexing the accumulators with a runtime strip, or branching per
+// side, moves them to scratch memory).
+
+// exchange slot of (direction, strip i of the half, fragment j) for this lane's pair
+__device__ __forceinline__ int swg_slot(int pair, int dir, int i, int j, int TH, int TN, int l) {
+  return ((pair * 2 + dir) * TH * TN + i * TN + j) * 64 + l;
+}
+
+// q = e4m3(h / s) for this wave's strips, staged in sQ ([rows][128] bytes; the 16-byte chunk
+// c of row r sits at chunk c ^ (r & 7), which spreads LDS banks).
+// The quotient is the correctly rounded fp32 h / s, from the row's reciprocal r = RN(1/s)
+// and Markstein's correction step (q0 = RN(h r), e = h - s q0 exact by FMA,
+// q = RN(q0 + e r)); that step is exact unless the residual underflows, so rows with
+// s < 2^-80 divide. Power-of-two scales: h r is the exact quotient. s == 0: signed zeros.
+// The hardware conversion (round to nearest even) is exact for |x| <= 448.0001, the range
+// h / s stays in. A 4x4 byte transpose over each lane quad turns the four row codes of a
+// lane into four column codes of one row.
+template <int TH, int TN, int WM, Layout L, bool kPow2>
+__device__ __forceinline__ void swg_quant(const v4f (&hv)[TH][TN], const float* sS, const float* sR, uint8_t* sQ,
+                                          int strip0, int wm, int half, int l, int act) {
+  const int fr = l & 15, g4 = l >> 4;
+  const int k4 = fr & 3, c4 = fr >> 2;
+  const uint32_t selA = (fr & 2) ? 0x03020706u : 0x05040100u;
+  const uint32_t selB = (fr & 1) ? 0x03070105u : 0x06020400u;
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    if (L == Layout::Masked && strip0 + i >= act) continue;
+    const int rb = ((strip0 + i) * WM + wm) * 16 + 4 * g4;
+    const float4 s4 = *reinterpret_cast<const float4*>(sS + rb);
+    const float4 r4 = *reinterpret_cast<const float4*>(sR + rb);
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+    constexpr float kTiny = 0x1p-80f;
+    const bool fast = kPow2 || (s4.x >= kTiny && s4.y >= kTiny && s4.z >= kTiny && s4.w >= kTiny);
+    const bool all_fast = __all(fast);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float h = hv[i][j][r];
+        if (kPow2) {
+          x[r] = h * rv[r];
+        } else if (all_fast) {
+          const float q0 = h * rv[r];
+          x[r] = fmaf(fmaf(-q0, sv[r], h), rv[r], q0);
+        } else {
+          const float q0 = h * rv[r];
+          x[r] = sv[r] == 0.0f ? h * 0.0f : (sv[r] >= kTiny ? fmaf(fmaf(-q0, sv[r], h), rv[r], q0) : h / sv[r]);
+        }
+      }
+      uint32_t P = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      P = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], (int)P, true);
+      uint32_t Q = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0x4E, 0xF, 0xF, true);  // lane ^ 2
+      P = __builtin_amdgcn_perm(Q, P, selA);
+      Q = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0xB1, 0xF, 0xF, true);           // lane ^ 1
+      P = __builtin_amdgcn_perm(Q, P, selB);
+      const int row = rb + k4, chunk = half * TN + j;
+      *reinterpret_cast<uint32_t*>(sQ + row * (int)kQ + ((chunk ^ (row & 7)) << 4) + 4 * c4) = P;
+    }
+  }
+}
+
 template <int BM, int WM, int WN, int TM, int TN, Layout L, bool kPow2>
 __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM][TN], uint8_t* smem, int g, int tn,
                                                 int64_t m0, int64_t valid, int act) {
   constexpr int NW = WM * WN, NT = 64 * NW;
-  constexpr int HF = TN / 2;                 // h fragments (16 columns each) per wave
-  constexpr int PART = WN * 16;              // partial maxima per row: one per (wave column, lane column)
+  constexpr int TH = TM / 2;                 // strips each wave of a pair finishes
+  constexpr int PART = 2 * 16;               // partial maxima per row: (column half, lane column)
   constexpr int PST = BM + 4;                // padded stride of a partial column (spreads LDS banks)
   constexpr int TPR = NT / BM;               // threads reducing one row
+  static_assert(WN == 4 && TN * 16 * 2 == (int)kQ, "two column halves of 64 per operand");
   static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0 && PART % TPR == 0, "row reduction split");
-  static_assert(HF * 16 * WN == (int)kQ, "a tile holds one 128-column block of h");
-  float* sAm = reinterpret_cast<float*>(smem);  // [PART][PST]
-  float* sS = sAm + PART * PST;                 // [BM] row scales
-  uint8_t* sQ = reinterpret_cast<uint8_t*>(sS + BM);  // [BM][128] codes
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w % WM, wn = w / WM;
   const int fr = l & 15, g4 = l >> 4;
+  const bool up_side = wn >= 2;
+  const int half = wn & 1;                   // which 64 of the 128 h columns
+  const int pair = wm * 2 + half;
   const int64_t I = p.N / 2;
 
+  v4f* sX = reinterpret_cast<v4f*>(smem);   // [pairs][direction][TH][TN][64 lanes]
+  const int strip0 = up_side ? TH : 0;       // the strips this wave finishes: strip0 .. +TH
   __syncthreads();  // every wave is past its last read of the LDS ring
+  // the gate wave sends its gate values of strips TH.., the up wave its up values of strips 0..TH-1
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (L == Layout::Masked && i >= act) continue;
-    float pm[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < TH; ++i) {
+    if (L == Layout::Masked && (TH - strip0) + i >= act) continue;
 #pragma unroll
-    for (int jj = 0; jj < HF; ++jj)
+    for (int j = 0; j < TN; ++j) sX[swg_slot(pair, up_side, i, j, TH, TN, l)] = up_side ? acc[i][j] : acc[TH + i][j];
+  }
+  __syncthreads();
+  // h for strips strip0.. from this wave's accumulators and the partner's
+  v4f hv[TH][TN];
+  float pm[TH][4];
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pm[i][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) hv[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (L == Layout::Masked && strip0 + i >= act) continue;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v4f other = sX[swg_slot(pair, !up_side, i, j, TH, TN, l)];
+      const v4f mine = up_side ? acc[TH + i][j] : acc[i][j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float h = swiglu1(acc[i][jj][r], acc[i][jj + HF][r]);
-        acc[i][jj][r] = h;
-        pm[r] = fmaxf(pm[r], fabsf(h));
+        const float h = swiglu1(up_side ? other[r] : mine[r], up_side ? mine[r] : other[r]);
+        hv[i][j][r] = h;
+        pm[i][r] = fmaxf(pm[i][r], fabsf(h));
       }
-    *reinterpret_cast<float4*>(sAm + (wn * 16 + fr) * PST + (i * WM + wm) * 16 + 4 * g4) =
-        make_float4(pm[0], pm[1], pm[2], pm[3]);
+    }
+  }
+  __syncthreads();  // the exchange area is reused below
+
+  float* sAm = reinterpret_cast<float*>(smem);  // [PART][PST]
+  float* sS = sAm + PART * PST;                 // [BM] row scales
+  float* sR = sS + BM;                          // [BM] their reciprocals
+  uint8_t* sQ = reinterpret_cast<uint8_t*>(sR + BM);  // [BM][128] codes
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    const int si = strip0 + i;
+    if (L == Layout::Masked && si >= act) continue;
+    *reinterpret_cast<float4*>(sAm + (half * 16 + fr) * PST + (si * WM + wm) * 16 + 4 * g4) =
+        make_float4(pm[i][0], pm[i][1], pm[i][2], pm[i][3]);
   }
   __syncthreads();
   {
@@ -1058,10 +1153,11 @@ __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM]
 #pragma unroll
     for (int k = 0; k < PART / TPR; ++k) am = fmaxf(am, sAm[(part * (PART / TPR) + k) * PST + row]);
 #pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) am = fmaxf(am, __shfl_xor(am, off, TPR));
+    for (int o = 1; o < TPR; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, TPR));
     const float s = kPow2 ? pow2_ceil(am / 448.0f) : am / 448.0f;
     if (part == 0) {
       sS[row] = s;
+      sR[row] = 1.0f / s;
       if (m0 + row < valid) {
         float* SH = p.sh + (L == Layout::Masked ? (int64_t)g * (I / kQ) * p.M : 0);
         SH[(int64_t)tn * p.M + m0 + row] = s;
@@ -1069,21 +1165,7 @@ __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM]
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (L == Layout::Masked && i >= act) continue;
-    const int rb = (i * WM + wm) * 16 + 4 * g4;
-    const float4 s4 = *reinterpret_cast<const float4*>(sS + rb);
-    const float sr[4] = {s4.x, s4.y, s4.z, s4.w};
-#pragma unroll
-    for (int jj = 0; jj < HF; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float h = acc[i][jj][r];
-        const uint32_t code = sr[r] == 0.0f ? ((__float_as_uint(h) >> 24) & 0x80u) : e4m3_encode(h / sr[r]);
-        sQ[(rb + r) * (int)kQ + wn * (HF * 16) + jj * 16 + fr] = (uint8_t)code;
-      }
-  }
+  swg_quant<TH, TN, WM, L, kPow2>(hv, sS, sR, sQ, strip0, wm, half, l, act);
   __syncthreads();
   uint8_t* HQ = p.hq + (L == Layout::Masked ? (int64_t)g * p.M * I : 0);
 #pragma unroll
@@ -1091,7 +1173,7 @@ __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM]
     const int row = idx >> 3, c16 = idx & 7;
     if (m0 + row < valid)
       *reinterpret_cast<uint4*>(HQ + (m0 + row) * I + (int64_t)tn * kQ + c16 * 16) =
-          *reinterpret_cast<const uint4*>(sQ + row * (int)kQ + c16 * 16);
+          *reinterpret_cast<const uint4*>(sQ + row * (int)kQ + ((c16 ^ (row & 7)) << 4));
   }
 }
 
@@ -1113,11 +1195,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
   static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
   static_assert(STAGES * STAGE_BYTES + NB * kMaxKb3 * 4 <= 160 * 1024, "LDS");
-  static_assert(!kSwiglu || (BN == 2 * (int)kQ && TN % 2 == 0), "SwiGLU tile: 128 gate + 128 up rows");
-  static_assert(!kSwiglu || WN * 16 * (BM + 4) * 4 + BM * 4 + BM * (int)kQ <= STAGES * STAGE_BYTES,
+  static_assert(!kSwiglu || (BN == 2 * (int)kQ && TM % 2 == 0), "SwiGLU tile: 128 gate + 128 up rows");
+  static_assert(!kSwiglu || (32 * (BM + 4) * 4 + BM * 8 + BM * (int)kQ <= STAGES * STAGE_BYTES &&
+                             BM * BN * 2 <= STAGES * STAGE_BYTES),
                 "SwiGLU epilogue fits in the LDS ring");
-  constexpr int NH = kSwiglu ? 2 : 1;  // weight-scale blocks a wave's fragments span
-  constexpr int FPH = TN / NH;         // fragments per scale block
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) float sSB[NB][kMaxKb3];  // this tile's weight scales
 
@@ -1212,19 +1293,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   // interleave by strips, so a partly valid tile (masked layout) leaves every wave a
   // similar number of active strips
   const uint32_t a_lane = (uint32_t)((wm * 16 + fr) * kQ);
-  // a wave's columns: WTN consecutive tile rows of B, or (SwiGLU) WTN/2 gate rows and the
-  // same WTN/2 up rows; fragment j reads tile rows frag_row(j) + wave offset + fr
-  const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * (WTN / NH) + fr) * kQ);
-  auto frag_row = [](int j) { return kSwiglu ? (j / FPH) * (int)kQ + (j % FPH) * 16 : j * 16; };
+  const uint32_t b_lane = (uint32_t)(BM * kQ + (wn * WTN + fr) * kQ);
   const uint32_t s_lane = (uint32_t)((BM + BN) * kQ + (wm * 16 + 4 * g4) * 4);
-  const int wnb = kSwiglu ? 0 : (wn * WTN) / (int)kQ;  // weight-scale block of fragment 0
+  const int wnb = (wn * WTN) / (int)kQ;  // this wave's weight-scale column block
 
   auto read_b = [&](v8i (&bf)[TN], int stage) {
     const uint8_t* b_s = smem + stage * STAGE_BYTES + b_lane;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bf[j] = cat8(*reinterpret_cast<const v4i*>(b_s + frag_row(j) * kQ + sw0),
-                   *reinterpret_cast<const v4i*>(b_s + frag_row(j) * kQ + sw1));
+      bf[j] = cat8(*reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw0),
+                   *reinterpret_cast<const v4i*>(b_s + j * 16 * kQ + sw1));
   };
   auto read_a = [&](v8i& af, float4& s4, int stage, int i) {
     const uint8_t* st = smem + stage * STAGE_BYTES;
@@ -1234,11 +1312,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   };
 
   v4f pp[2][TN];
-  float4 tt[2][NH];
+  float4 tt[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
-#pragma unroll
-    for (int h = 0; h < NH; ++h) tt[q][h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    tt[q] = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < TN; ++j) pp[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -1251,9 +1328,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   }
   auto promote = [&](int slot, int strip) {
     if (L == Layout::Masked && strip >= act) return;
+    const float4 tp = tt[slot];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const float4 tp = tt[slot][j / FPH];
       acc[strip][j][0] = fmaf(pp[slot][j][0], tp.x, acc[strip][j][0]);
       acc[strip][j][1] = fmaf(pp[slot][j][1], tp.y, acc[strip][j][1]);
       acc[strip][j][2] = fmaf(pp[slot][j][2], tp.z, acc[strip][j][2]);
@@ -1285,9 +1362,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   // next K block's fragments (stage `sn`) replace them, B as the last strip's MFMAs
   // consume it
   auto kblock = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, float4& s0) {
-    float sb[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) sb[h] = sSB[wnb + h][kb];
+    const float sb = sSB[wnb][kb];
     v8i af[2];
     float4 s4[2];
     af[0] = a0;
@@ -1297,8 +1372,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       const int c = i & 1;
       read_a(af[c ^ 1], s4[c ^ 1], st, i + 1);
       strip(af[c], bf, c, i, i == 0 ? TM - 1 : i - 1);  // strip 0 promotes the previous K block's last
-#pragma unroll
-      for (int h = 0; h < NH; ++h) tt[c][h] = factor(s4[c], sb[h]);
+      tt[c] = factor(s4[c], sb);
     }
     // every read of stage st is issued; wait for the next stage, then recycle stage st
     __builtin_amdgcn_sched_barrier(0);
@@ -1319,8 +1393,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
-#pragma unroll
-    for (int h = 0; h < NH; ++h) tt[1][h] = factor(s4[1], sb[h]);
+    tt[1] = factor(s4[1], sb);
   };
 
   // power-of-two scales: the matrix unit applies them. Lane l supplies the E8M0 scale of
@@ -1335,9 +1408,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     ea = (int)(*reinterpret_cast<const uint32_t*>(st + e_lane + 64 * WM * i) >> 23);
   };
   auto kblock2 = [&](int kb, int st, int sn, v8i (&bf)[TN], v8i& a0, int& e0) {
-    int eb[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) eb[h] = (int)(__float_as_uint(sSB[wnb + h][kb]) >> 23);
+    const int eb = (int)(__float_as_uint(sSB[wnb][kb]) >> 23);
     v8i af[2];
     int ea[2];
     af[0] = a0;
@@ -1349,7 +1420,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         if (!(L == Layout::Masked && i >= act))
-          acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb[j / FPH]);
+          acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -1359,7 +1430,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       if (!(L == Layout::Masked && TM - 1 >= act))
-        acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb[j / FPH]);
+        acc[TM - 1][j] = mfma_f8_16x16x128_scaled(af[1], bf[j], acc[TM - 1][j], ea[1], eb);
     read_b(bf, sn);
 #pragma unroll
     for (int j = 0; j < TN; ++j) {

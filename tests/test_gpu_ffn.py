@@ -196,23 +196,27 @@ def _exact_codes(rng, shape, exp_field):
     return sign | np.uint8(exp_field << 3) | mant
 
 
-@pytest.mark.parametrize("pow2", [False, True])
-def test_swiglu_epilogue_on_exact_accumulators(dg, pow2):
+@pytest.mark.parametrize("pow2,shift", [(False, 0), (True, 0), (False, -45), (True, -45)])
+def test_swiglu_epilogue_on_exact_accumulators(dg, pow2, shift):
     # codes and power-of-two scales chosen so that every block sum and every promoted
     # partial is exact in fp32: the kernel's gate/up equal the oracle's, and the only
-    # freedom left is the fp32 evaluation of silu (band (|g| + 16) 2^-22 |h|)
+    # freedom left is the fp32 evaluation of silu (band (|g| + 16) 2^-22 |h|). shift -45
+    # makes h ~ 2^-91 and its scales ~ 2^-100: the path that divides instead of using the
+    # reciprocal correction step.
     G, H, I = 2, 512, 256
     rng = np.random.default_rng(91)
     mi = np.repeat(np.arange(G, dtype=np.int32), 128)
     M = mi.size
     xq = _exact_codes(rng, (M, H), 7)                     # |x| in [1, 2)
     w1q = _exact_codes(rng, (G, 2 * I, H), 4)             # |w| in [1/8, 1/4)
-    sx = np.ldexp(1.0, rng.integers(-2, 1, size=(M, H // 128))).astype(np.float32)
+    sx = np.ldexp(1.0, rng.integers(-2, 1, size=(M, H // 128)) + shift).astype(np.float32)
     s1 = np.ldexp(1.0, rng.integers(-1, 1, size=(G, 2 * I // 128, H // 128))).astype(np.float32)
     w2q = _exact_codes(rng, (G, H, I), 4)
     s2 = np.ones((G, H // 128, I // 128), np.float32)
     ref = oracle.moe_ffn_contiguous(xq, sx, w1q, s1, w2q, s2, mi, pow2)
-    say("swiglu exact accumulators ue8m0=%d" % pow2)
+    say("swiglu exact accumulators ue8m0=%d shift=%d" % (pow2, shift))
+    if shift:
+        assert np.nanmax(ref["sh"]) < 2.0 ** -80 and np.nanmin(ref["sh"]) > 0
     hq_d, sh_d = dg.gemm_fp8_swiglu(CONTIG, to_dev(xq), to_dev(kmajor(sx)), to_dev(w1q), to_dev(s1), to_dev(mi),
                                     ue8m0=pow2)
     torch.cuda.synchronize()
@@ -224,6 +228,7 @@ def test_swiglu_epilogue_on_exact_accumulators(dg, pow2):
 
 
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("layout", ["contiguous", "masked"])
 def test_ffn_full_size_sampled(dg, layout):
     # the bench's FFN shapes: hidden 7168, expert intermediate 2048; the oracle checks a
@@ -261,6 +266,7 @@ def test_ffn_full_size_sampled(dg, layout):
     for e, rows in rows_all.items():
         if len(rows) == 0:
             continue
+        say("  expert %d: %d sampled rows" % (e, min(per, len(rows))))
         pick = np.sort(rng.choice(rows, size=min(per, len(rows)), replace=False))
         sub = oracle.moe_ffn_contiguous(xf[pick], sxf[pick], w1q[e:e + 1], s1[e:e + 1], w2q[e:e + 1], s2[e:e + 1],
                                         np.zeros(len(pick), np.int32))
