@@ -177,6 +177,27 @@ def test_swiglu_dense(dg):
                 bf16_values(y_d), False, "ffn dense")
 
 
+def test_ffn_masked_counts_are_clamped(dg):
+    # masked_m outside [0, M_max]: negative counts as 0, larger as M_max
+    G, M_max, H, I = 3, 96, 256, 128
+    say("ffn masked clamped counts")
+    mm = np.array([-5, 500, 40], np.int32)
+    dev, (xq, sx, w1q, s1, w2q, s2, _), _ = _masked_case(dg, G, M_max, H, I, 81, False, mm)
+    ref = oracle.moe_ffn_masked(xq, sx, w1q, s1, w2q, s2, mm)
+    xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d = dev
+    hq_d = torch.full((G, M_max, I), SENTINEL_Q, dtype=torch.uint8, device="cuda")
+    y_d = torch.full((G, M_max, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    _, _, sh_d = dg.moe_ffn_fp8(MASKED, xq_d, sx_d, w1_d, s1_d, w2_d, s2_d, mm_d, hq=hq_d, y=y_d)
+    torch.cuda.synchronize()
+    hq = hq_d.cpu().numpy()
+    assert np.all(hq[0] == SENTINEL_Q) and np.all(hq[2, 40:] == SENTINEL_Q) and not np.any(hq[1] == SENTINEL_Q)
+    counts = [0, M_max, 40]
+    rows = {g: g * M_max + np.arange(counts[g]) for g in range(G)}
+    sh = kmajor(sh_d.cpu().numpy()).reshape(-1, I // 128)
+    _check_rows(rows, xq.reshape(-1, H), sx.reshape(-1, H // 128), w1q, s1, w2q, s2, _flat(ref), hq.reshape(-1, I),
+                sh, bf16_values(y_d).reshape(-1, H), False, "ffn masked clamped")
+
+
 def test_ffn_masked_all_empty(dg):
     G, M_max, H, I = 3, 64, 128, 128
     say("ffn masked all groups empty")

@@ -83,3 +83,51 @@ def test_grouped_graph_replays_match_eager(dg):
         rows = np.concatenate([gg * Mm + np.arange(int(mm[gg])) for gg in range(G)])
         dv, rv = d.view(G * Mm, N)[rows], ref.view(G * Mm, N)[rows]
         assert torch.equal(dv.view(torch.int16), rv.view(torch.int16)), "replay %d" % r
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "masked"])
+def test_ffn_graph_replays_match_eager(dg, layout):
+    # token cast + expert FFN (fused gate/up + SwiGLU + re-cast, then the down GEMM)
+    dev = torch.device("cuda:0")
+    G, H, I = 3, 384, 256
+    if layout == "contiguous":
+        mi, _ = synth.contiguous_layout(G, 300, 5)
+        x32 = synth.normal((mi.size, H), 5, synth.TID_A)
+        x32[mi < 0] = 0.0
+        meta = torch.from_numpy(mi).to(dev)
+        lay, sx_shape, rows = dg.LAYOUT_CONTIGUOUS, (H // 128, mi.size), (mi.size,)
+    else:
+        mm = np.array([70, 0, 128], np.int32)
+        x32 = synth.normal((G, 128, H), 5, synth.TID_A)
+        meta = torch.from_numpy(mm).to(dev)
+        lay, sx_shape, rows = dg.LAYOUT_MASKED, (G, H // 128, 128), (G, 128)
+    w1, w2 = synth.ffn_weights(G, H, I, 5)
+    q1, s1 = dg.cast_fp8_per_block(torch.from_numpy(w1.reshape(-1, H)).to(dev))
+    q2, s2 = dg.cast_fp8_per_block(torch.from_numpy(w2.reshape(-1, I)).to(dev))
+    q1, s1 = q1.view(G, 2 * I, H), s1.view(G, 2 * I // 128, H // 128)
+    q2, s2 = q2.view(G, H, I), s2.view(G, H // 128, I // 128)
+    x = torch.from_numpy(x32).to(dev)
+    qx = torch.empty(tuple(x.shape), dtype=torch.uint8, device=dev)
+    sx = torch.empty(sx_shape, dtype=torch.float32, device=dev)
+    hq = torch.zeros(rows + (I,), dtype=torch.uint8, device=dev)
+    sh = torch.zeros((G, I // 128, 128) if layout == "masked" else (I // 128, mi.size), dtype=torch.float32,
+                     device=dev)
+    y = torch.zeros(rows + (H,), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        dg.cast_fp8_per_token(x, qx, sx)
+        dg.moe_ffn_fp8(lay, qx, sx, q1, s1, q2, s2, meta, expected_m=64, hq=hq, sfh=sh, y=y)
+
+    say("graph replay ffn %s" % layout)
+    step()
+    torch.cuda.synchronize()
+    hq_ref, sh_ref, y_ref = hq.clone(), sh.clone(), y.clone()
+    g = _capture(step)
+    for r in range(3):
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hq, hq_ref), "replay %d: h codes" % r
+        assert torch.equal(sh.view(torch.int32), sh_ref.view(torch.int32)), "replay %d: h scales" % r
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), "replay %d: y" % r
+        qx.fill_(0); sx.fill_(-1.0)   # eager work between replays (recomputed by the next replay)
