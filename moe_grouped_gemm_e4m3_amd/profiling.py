@@ -10,6 +10,13 @@
       from two separate --pmc runs), each scaled by what the same counter reads for the
       reference copy kernel (a 256 MiB device-to-device copy, 256 MiB read and written).
 
+  python -m moe_grouped_gemm_e4m3_amd.profiling mfma DIR [--se 32] [--simds 1024]
+      per kernel and grid: FP8 MFMA work counted by the hardware (SQ_INSTS_VALU_MFMA_MOPS_F8
+      and _F6F4, 512 flops per unit), MFMA instructions, and the matrix-unit utilisation
+      SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), averaged over dispatches. The SQ
+      counters read per shader engine; totals are scaled by the engine count (32 on MI355X:
+      8 XCDs x 4), which the flop totals confirm against the algorithmic counts.
+
 Nothing here touches the GPU; it only reads the databases rocprofv3 wrote.
 """
 from __future__ import annotations
@@ -66,6 +73,21 @@ def pmc_stats(path: str):
     return rows
 
 
+def mfma_stats(path: str):
+    """{(kernel, grid): {counter: average per dispatch}, plus the dispatch count}."""
+    acc = {}
+    for db in _dbs(path):
+        c = sqlite3.connect(db)
+        rows = c.execute("select p.name, k.grid_x, p.counter_name, avg(p.counter_value), count(*) from pmc_events p "
+                         "left join kernels k on k.dispatch_id = p.dispatch_id "
+                         "group by p.name, k.grid_x, p.counter_name").fetchall()
+        for name, grid, counter, v, n in rows:
+            rec = acc.setdefault((name, grid), {})
+            rec[counter] = v
+            rec["n"] = max(rec.get("n", 0), n)
+    return acc
+
+
 def _counter_per_kernel(path: str, counter: str, regex: str, grid=None, largest=False):
     vals = []
     for db in _dbs(path):
@@ -113,6 +135,9 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     p = sub.add_parser("stats"); p.add_argument("path"); p.add_argument("--match", default="")
     p = sub.add_parser("pmc"); p.add_argument("path"); p.add_argument("--match", default="")
+    p = sub.add_parser("mfma"); p.add_argument("path"); p.add_argument("--match", default="")
+    p.add_argument("--se", type=int, default=32)
+    p.add_argument("--simds", type=int, default=1024)
     p = sub.add_parser("traffic")
     for a in ("--fetch", "--write", "--workload", "--label", "--kernel", "--out"):
         p.add_argument(a, required=True)
@@ -129,6 +154,19 @@ def main(argv=None):
             if args.match and not re.search(args.match, name):
                 continue
             print("%-34s %18.1f  n=%-4d dur=%9.3fus  %s" % (counter, v, n, dur / 1e3, _short(name)))
+    elif args.cmd == "mfma":
+        print("%6s %9s %11s %11s %11s %12s %12s %7s  %s" % (
+            "calls", "grid", "F8 GFLOP", "F6F4 GFLOP", "MFMA insts", "busy cyc/SE", "active cyc", "util %", "kernel"))
+        for (name, grid), rec in sorted(mfma_stats(args.path).items(), key=lambda kv: _short(kv[0][0])):
+            if args.match and not re.search(args.match, name):
+                continue
+            f8 = rec.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512 * args.se / 1e9
+            f64 = rec.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0.0) * 512 * args.se / 1e9
+            busy, act = rec.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), rec.get("GRBM_GUI_ACTIVE", 0.0)
+            util = 100.0 * busy * args.se / (act * args.simds) if act else 0.0
+            print("%6d %9s %11.3f %11.3f %11.0f %12.4g %12.4g %7.1f  %s" % (
+                rec.get("n", 0), grid, f8, f64, rec.get("SQ_INSTS_VALU_MFMA_F8", 0.0) * args.se, busy, act, util,
+                _short(name)))
     else:
         print(json.dumps(traffic(args), indent=1))
 
