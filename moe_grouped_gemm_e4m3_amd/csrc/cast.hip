@@ -40,10 +40,10 @@ __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
 }
 
 // 32 lanes per 128-element chunk, 4 elements per lane; a 256-thread block covers 8
-// chunks per pass and walks the chunks grid-stride. Chunks are numbered in the order of
-// the scale tensor [G][K/128][M] (row fastest): chunk c is row r = c % M, K block
-// kb = (c / M) % (K/128), group g = c / (M * K/128), so sf[c] is its own scale and the 8
-// scales of a pass are 32 contiguous bytes. Idx is uint32_t when the chunk count fits.
+// chunks per pass and walks the chunks grid-stride. Chunks are numbered in input order
+// (K block fastest), so the 8 chunks of a pass are 4 KB (fp32) of contiguous input; each
+// scale goes to its place in the K-block-major tensor [G][K/128][M]. Idx is uint32_t when
+// the chunk count fits.
 template <bool kBf16, bool kPow2, typename Idx>
 __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x, Idx nchunks,
                                                              Idx M, Idx kblocks, uint8_t* __restrict__ q,
@@ -51,9 +51,10 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restr
   const int lane = threadIdx.x & 31;
   const int64_t K = (int64_t)kblocks * kQ;
   for (Idx c = (Idx)blockIdx.x * 8 + (Idx)(threadIdx.x >> 5); c < nchunks; c += (Idx)gridDim.x * 8) {
-    const Idx gk = c / M, r = c - gk * M;
-    const Idx g = gk / kblocks, kb = gk - g * kblocks;
-    const int64_t e0 = ((int64_t)g * (int64_t)M + (int64_t)r) * K + (int64_t)kb * kQ + lane * 4;
+    // chunk c in input order: row-major over (group, row), K block fastest
+    const Idx gr = c / kblocks, kb = c - gr * kblocks;
+    const Idx g = gr / M, r = gr - g * M;
+    const int64_t e0 = (int64_t)c * kQ + lane * 4;
     float v[4];
     load4<kBf16>(x, e0, v);
     float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restr
     for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
     const float s = kPow2 ? pow2_ceil(amax / 448.0f) : amax / 448.0f;
     *reinterpret_cast<uint32_t*>(q + e0) = quant4(v, s);
-    if (lane == 0) sf[c] = s;
+    if (lane == 0) sf[((int64_t)g * kblocks + kb) * M + r] = s;
   }
 }
 
