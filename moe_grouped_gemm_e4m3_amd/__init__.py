@@ -222,7 +222,7 @@ def grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m: int = 0, d: torch.
 
 
 # ---- expert FFN ------------------------------------------------------------------------
-def _ffn_shapes(layout, a, sfa, w1, meta):
+def _ffn_shapes(layout, a, sfa, w1, sfw1, meta):
     """Checks the gate/up operands; returns (G, M, K, I) and the hq / sfh shapes."""
     if layout == LAYOUT_MASKED:
         G, M, K = a.shape
@@ -234,8 +234,10 @@ def _ffn_shapes(layout, a, sfa, w1, meta):
     two_i = w1.shape[-2]
     I = two_i // 2
     want_w1 = (G, two_i, K) if (layout != LAYOUT_DENSE or w1.dim() == 3) else (two_i, K)
-    if tuple(sfa.shape) != want_sfa or tuple(w1.shape) != want_w1 or two_i % 2:
-        raise ValueError("shape mismatch: a %s sfa %s w1 %s" % (tuple(a.shape), tuple(sfa.shape), tuple(w1.shape)))
+    want_s1 = want_w1[:-2] + (two_i // 128, K // 128)
+    if tuple(sfa.shape) != want_sfa or tuple(w1.shape) != want_w1 or two_i % 2 or tuple(sfw1.shape) != want_s1:
+        raise ValueError("shape mismatch: a %s sfa %s w1 %s sfw1 %s" % (tuple(a.shape), tuple(sfa.shape),
+                                                                       tuple(w1.shape), tuple(sfw1.shape)))
     if layout == LAYOUT_CONTIGUOUS and (meta is None or tuple(meta.shape) != (M,)):
         raise ValueError("contiguous layout needs m_indices [M_total]")
     if layout == LAYOUT_MASKED and (meta is None or tuple(meta.shape) != (G,)):
@@ -251,7 +253,7 @@ def gemm_fp8_swiglu(layout, a, sfa, w1, sfw1, meta=None, expected_m: int = 0, hq
     then up rows), sfw1 [G,2I/128,K/128]; returns hq (e4m3 [rows,I]) and sfh ([I/128,rows]),
     with a leading [G] for the masked layout."""
     _operands(a, sfa, w1, sfw1)
-    G, M, K, I, hq_shape, sh_shape = _ffn_shapes(layout, a, sfa, w1, meta)
+    G, M, K, I, hq_shape, sh_shape = _ffn_shapes(layout, a, sfa, w1, sfw1, meta)
     if meta is not None:
         _need(meta, torch.int32, "meta")
     hq = torch.empty(hq_shape, dtype=torch.uint8, device=a.device) if hq is None else hq
@@ -274,9 +276,9 @@ def moe_ffn_fp8(layout, x, sfx, w1, sfw1, w2, sfw2, meta=None, expected_m: int =
     _operands(x, sfx, w1, sfw1)
     _need(w2, torch.uint8, "w2")
     _need(sfw2, torch.float32, "sfw2")
-    G, M, H, I, hq_shape, sh_shape = _ffn_shapes(layout, x, sfx, w1, meta)
+    G, M, H, I, hq_shape, sh_shape = _ffn_shapes(layout, x, sfx, w1, sfw1, meta)
     want_w2 = (G, H, I) if (layout != LAYOUT_DENSE or w2.dim() == 3) else (H, I)
-    if tuple(w2.shape) != want_w2 or tuple(sfw2.shape)[-2:] != (H // 128, I // 128):
+    if tuple(w2.shape) != want_w2 or tuple(sfw2.shape) != want_w2[:-2] + (H // 128, I // 128):
         raise ValueError("shape mismatch: w2 %s sfw2 %s" % (tuple(w2.shape), tuple(sfw2.shape)))
     if meta is not None:
         _need(meta, torch.int32, "meta")

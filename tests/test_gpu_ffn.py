@@ -294,3 +294,28 @@ def test_ffn_full_size_sampled(dg, layout):
         local = {0: np.arange(len(pick))}
         _check_rows(local, xf[pick], sxf[pick], w1q[e:e + 1], s1[e:e + 1], w2q[e:e + 1], s2[e:e + 1], sub,
                     hq[pick], sh[pick], y[pick], False, "ffn full %s expert %d" % (layout, e))
+
+
+def test_ffn_binding_rejects_bad_shapes(dg):
+    # shape errors are caught before anything is launched
+    G, H, I, M = 2, 256, 128, 128
+    d = torch.device("cuda:0")
+    x = torch.zeros((M, H), dtype=torch.uint8, device=d)
+    sx = torch.ones((H // 128, M), dtype=torch.float32, device=d)
+    w1 = torch.zeros((G, 2 * I, H), dtype=torch.uint8, device=d)
+    s1 = torch.ones((G, 2 * I // 128, H // 128), dtype=torch.float32, device=d)
+    w2 = torch.zeros((G, H, I), dtype=torch.uint8, device=d)
+    s2 = torch.ones((G, H // 128, I // 128), dtype=torch.float32, device=d)
+    mi = torch.zeros((M,), dtype=torch.int32, device=d)
+    say("ffn binding shape checks")
+    with pytest.raises(ValueError):
+        dg.gemm_fp8_swiglu(CONTIG, x, sx, w1, s1[:, :1], mi)
+    with pytest.raises(ValueError):
+        dg.moe_ffn_fp8(CONTIG, x, sx, w1, s1, w2, s2[:1], mi)
+    with pytest.raises(ValueError):
+        dg.moe_ffn_fp8(CONTIG, x, sx.t().contiguous(), w1, s1, w2, s2, mi)
+    with pytest.raises(ValueError):
+        dg.moe_ffn_fp8(MASKED, x, sx, w1, s1, w2, s2, mi)
+    y, hq, sh = dg.moe_ffn_fp8(CONTIG, x, sx, w1, s1, w2, s2, mi)  # well-formed: runs
+    torch.cuda.synchronize()
+    assert torch.all(hq == 0) and torch.all(y.float() == 0)
