@@ -16,7 +16,8 @@ stream it runs on. `cpu_baseline` is the CPU oracle on the host cores over a bou
 of the same workload. `traffic` (HBM bytes per launch) is read from profiles/traffic.json
 when that file was produced from the current kernel source.
 
-Other workloads (--workload prefill|contiguous|masked|tiny) print the same line shape.
+Other workloads (--workload prefill|contiguous|masked|ffn_contiguous|ffn_masked|ffn_masked_decode|tiny)
+print the same line shape.
 --ue8m0 runs the same steps with power-of-two (UE8M0) scales: the _ue8m0 casts and GEMMs.
 """
 from __future__ import annotations
@@ -57,9 +58,13 @@ WORKLOADS = {
                        "layers": [("ffn_contiguous", dict(G=8, tokens=8192, H=7168, I=2048))]},
     "ffn_masked": {"desc": "MoE expert FFN, masked G=32, M_max=256, valid ~U{0..256}: H=7168, I=2048",
                    "layers": [("ffn_masked", dict(G=32, M_max=256, H=7168, I=2048))]},
+    # decode-sized expert batches: 128 tokens x top-8 over 256 experts is 4 rows per expert on
+    # average; one GPU's 32 experts with valid rows ~U{0..8} in 64-row buffers
+    "ffn_masked_decode": {"desc": "MoE expert FFN at decode, masked G=32, M_max=64, valid ~U{0..8}: H=7168, I=2048",
+                          "layers": [("ffn_masked", dict(G=32, M_max=64, H=7168, I=2048, max_count=8))]},
 }
 FFN_KINDS = ("ffn_contiguous", "ffn_masked")
-FFN_WORKLOADS = ("ffn_contiguous", "ffn_masked")
+FFN_WORKLOADS = ("ffn_contiguous", "ffn_masked", "ffn_masked_decode")
 
 
 def weight_elems(kind, s):
@@ -131,7 +136,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
         meta = mi_d
         G = s["G"]
     else:
-        mm = synth.masked_layout(s["G"], s["M_max"], seed)
+        mm = synth.masked_layout(s["G"], s["M_max"], seed, s.get("max_count"))
         rows = s["G"] * s["M_max"]
         valid = int(mm.sum())
         a = torch.randn((s["G"], s["M_max"], K), generator=gen, device=dev, dtype=torch.float32)

@@ -1765,7 +1765,10 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
     if (p.layout == Layout::Dense)
       sched = p.M <= 64 ? Schedule::Decode : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
     else if (p.layout == Layout::Masked)
-      sched = (expected_m > 0 && expected_m <= 64) ? Schedule::Decode : Schedule::Tile256;
+      // the direct-load tiles at every count: at decode-sized counts they stream the weights
+      // at 5-6.4 TB/s where the decode schedule (one 64-row block per workgroup, weights
+      // re-streamed per block) reached 1.2-3.9 TB/s
+      sched = Schedule::Tile256;
     else
       sched = Schedule::Tile128;
   }
@@ -1822,7 +1825,10 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
           pick("tile2_256x128");
           return run_tile2<256, 128, 4, 2, Layout::Masked>(kp, stream);
         }
-        if (is("t3_128x256")) {
+        // 128-row tiles when most groups fit in one (each group's weights are then streamed
+        // once, with two LDS stages of them in flight); 256-row tiles otherwise
+        const bool small = p.M <= 128 || (expected_m > 0 && expected_m <= 64);
+        if (is("t3_128x256") || (!force && small)) {
           pick("tile3_128x256");
           const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Masked>(kp, stream);
           if (e != hipErrorNotSupported) return e;
@@ -1877,7 +1883,7 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
       pick("tile3_swiglu_128x256");
       return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true>(kp, stream);
     case Layout::Masked:
-      if (is("t3_128x256") || (!force && expected_m > 0 && expected_m <= 64)) {
+      if (is("t3_128x256") || (!force && (p.M <= 128 || (expected_m > 0 && expected_m <= 64)))) {
         pick("tile3_swiglu_128x256");
         return run_tile3<128, 256, 2, 4, 3, Layout::Masked, true>(kp, stream);
       }

@@ -15,7 +15,8 @@ Recipes (one generator stream per (seed, tensor id), numpy PCG64):
   * contiguous MoE layout: per-expert routed row counts ~ Multinomial(tokens, 1/G each),
     each expert's rows padded up to a multiple of 128; m_indices holds the expert id of
     each row, -1 on padding rows; padding rows of A are zero;
-  * masked MoE layout: valid rows per expert ~ uniform on {0, ..., M_max} (inclusive);
+  * masked MoE layout: valid rows per expert ~ uniform on {0, ..., M_max} (inclusive), or on
+    {0, ..., max_count} for decode-sized batches;
   * expert FFN weights: gate/up W1 [G, 2I, H] and down W2 [G, H, I], both ~ N(0, 0.02).
 """
 from __future__ import annotations
@@ -60,9 +61,10 @@ def contiguous_layout(G: int, tokens: int, seed: int, align: int = QBLK):
     return m_indices, counts.astype(np.int64)
 
 
-def masked_layout(G: int, M_max: int, seed: int) -> np.ndarray:
-    """masked_m [G] int32, each uniform on {0..M_max}."""
-    return rng(seed, TID_MASK).integers(0, M_max + 1, size=G).astype(np.int32)
+def masked_layout(G: int, M_max: int, seed: int, max_count: int | None = None) -> np.ndarray:
+    """masked_m [G] int32, each uniform on {0..max_count} (default max_count = M_max)."""
+    hi = M_max if max_count is None else min(int(max_count), M_max)
+    return rng(seed, TID_MASK).integers(0, hi + 1, size=G).astype(np.int32)
 
 
 # Workload catalogue: shapes and recipes of the five configurations.
