@@ -28,7 +28,9 @@ struct GemmProblem {
 
 // Kernel schedules. Decode: 64-row M blocks, K split across the waves of a workgroup,
 // operands streamed straight into registers. Tile: LDS-staged, double-buffered tiles.
-enum class Schedule : int { Auto = 0, Decode = 1, Tile128 = 2, Tile256 = 3 };
+// Tile64 (chosen internally for dense M <= 64, never passed in through the C ABI): 64x128
+// direct-load tiles.
+enum class Schedule : int { Auto = 0, Decode = 1, Tile128 = 2, Tile256 = 3, Tile64 = 4 };
 
 hipError_t launch_gemm(const GemmProblem& p, Schedule s, int64_t expected_m, hipStream_t stream,
                        const char** chosen);

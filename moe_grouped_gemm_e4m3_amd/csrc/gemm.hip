@@ -1193,7 +1193,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert((BN % kQ == 0 || kQ % BN == 0) && kQ % WTN == 0, "tile vs weight-scale blocks");
   static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
   static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
-  static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
+  static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 1) * PER_STAGE < 64, "LDS ring depth");
   static_assert(STAGES * STAGE_BYTES + NB * kMaxKb3 * 4 <= 160 * 1024, "LDS");
   static_assert(!kSwiglu || (BN == 2 * (int)kQ && TM % 2 == 0), "SwiGLU tile: 128 gate + 128 up rows");
   static_assert(!kSwiglu || (32 * (BM + 4) * 4 + BM * 8 + BM * (int)kQ <= STAGES * STAGE_BYTES &&
@@ -1762,8 +1762,15 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G; kp.pow2 = p.pow2;
 
   if (sched == Schedule::Auto) {
+    // dense M <= 64: 64x128 direct-load tiles when they make enough workgroups to cover the
+    // chip (measured 5% faster than the decode schedule on 64x24576x1536), else the decode
+    // schedule
     if (p.layout == Layout::Dense)
-      sched = p.M <= 64 ? Schedule::Decode : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
+      sched = p.M <= 64 ? (p.N % 128 == 0 && p.N / 128 >= 160 && !getenv("DG_DECODE") &&
+                                   !getenv("DG_DECODE2")
+                               ? Schedule::Tile64
+                               : Schedule::Decode)
+                        : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
     else if (p.layout == Layout::Masked)
       // the direct-load tiles at every count: at decode-sized counts they stream the weights
       // at 5-6.4 TB/s where the decode schedule (one 64-row block per workgroup, weights
@@ -1804,6 +1811,12 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         pick("tile3_128x256");
         const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Dense>(kp, stream);
         if (e != hipErrorNotSupported) return e;
+      }
+      if (sched == Schedule::Tile64 || is("t3_64x128")) {
+        pick("tile3_64x128");
+        const hipError_t e = run_tile3<64, 128, 2, 4, 3, Layout::Dense>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+        if (sched == Schedule::Tile64) return run_decode_auto<Layout::Dense>(kp, stream, chosen);
       }
       if (sched == Schedule::Tile256) {
         pick("tile3_256x256");

@@ -51,7 +51,7 @@ def test_decode_full_size(dg, N, K):
     d = dg.gemm_fp8_nt(qa, sa, qb, sb)
     R = oracle.gemm(oqa, osa, oqb, osb)
     assert_close(bf16_values(d), R, "decode %dx%d" % (N, K))
-    for sched in ("tile128", "tile256"):
+    for sched in ("decode", "tile128", "tile256"):
         d2 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES[sched])
         assert_close(bf16_values(d2), R, "decode %dx%d %s" % (N, K, sched))
 
@@ -155,7 +155,7 @@ def test_empty_problems_launch_nothing(dg):
 
 # every tile kernel, forced through DG_TILE (None = the automatic choice); they all sum the
 # K blocks in the same order with the same fp32 operations, so they must agree bit for bit
-TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256"]
+TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "t3_64x128"]
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 1280), (512, 256, 2304), (77, 768, 384), (1000, 640, 640),
