@@ -73,24 +73,26 @@ def weight_elems(kind, s):
     return s.get("G", 1) * s["N"] * s["K"]
 
 
-def swiglu_work(s, valid_rows):
-    """Flops and HBM bytes of the fused gate/up launch: A, W1 and their scales in; the FP8
-    activation h and its per-token scales out."""
-    G, H, I = s["G"], s["H"], s["I"]
+def swiglu_work(s, valid_rows, active):
+    """Flops and HBM bytes of the fused gate/up launch: A, the W1 of the `active` experts (those
+    with at least one valid row) and their scales in; the FP8 activation h and its per-token
+    scales out."""
+    H, I = s["H"], s["I"]
     flops = 2.0 * valid_rows * 2 * I * H
-    byts = (valid_rows * H + G * 2 * I * H + 4 * valid_rows * H // 128 + 4 * G * (2 * I // 128) * (H // 128)
-            + valid_rows * I + 4 * valid_rows * I // 128)
+    byts = (valid_rows * H + active * 2 * I * H + 4 * valid_rows * H // 128
+            + 4 * active * (2 * I // 128) * (H // 128) + valid_rows * I + 4 * valid_rows * I // 128)
     return flops, float(byts)
 
 
-def layer_work(kind, s, valid_rows):
-    """Algorithmic flops and HBM bytes of one GEMM launch (valid rows only)."""
+def layer_work(kind, s, valid_rows, active):
+    """Algorithmic flops and HBM bytes of one GEMM launch: valid rows only, and the weights of
+    the `active` groups only (an expert with no rows needs none of its weights)."""
     if kind in FFN_KINDS:  # the whole FFN: fused gate/up + down
-        f1, b1 = swiglu_work(s, valid_rows)
-        f2, b2 = layer_work(kind[4:], dict(G=s["G"], N=s["H"], K=s["I"]), valid_rows)
+        f1, b1 = swiglu_work(s, valid_rows, active)
+        f2, b2 = layer_work(kind[4:], dict(G=s["G"], N=s["H"], K=s["I"]), valid_rows, active)
         return f1 + f2, b1 + b2
     N, K = s["N"], s["K"]
-    G = s.get("G", 1)
+    G = active
     flops = 2.0 * valid_rows * N * K
     byts = (valid_rows * K            # A e4m3
             + G * N * K               # B e4m3
@@ -121,6 +123,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
     if base == "dense":
         rows = s["M"]
         valid = rows
+        active = 1
         a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
         if s.get("outliers"):
             hit = torch.rand((rows, K), generator=gen, device=dev) < 0.01
@@ -130,6 +133,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
         mi, counts = synth.contiguous_layout(s["G"], s["tokens"], seed)
         rows = mi.size
         valid = int(counts.sum())
+        active = int((counts > 0).sum())
         a = torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32)
         mi_d = torch.from_numpy(mi).to(dev)
         a[mi_d < 0] = 0.0
@@ -139,6 +143,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
         mm = synth.masked_layout(s["G"], s["M_max"], seed, s.get("max_count"))
         rows = s["G"] * s["M_max"]
         valid = int(mm.sum())
+        active = int((mm > 0).sum())
         a = torch.randn((s["G"], s["M_max"], K), generator=gen, device=dev, dtype=torch.float32)
         meta = torch.from_numpy(mm).to(dev)
         G = s["G"]
@@ -165,7 +170,7 @@ def build_layer(dg, torch, kind, s, seed, copies, ue8m0=False):
         d = torch.empty((s["G"], s["M_max"], N), dtype=torch.bfloat16, device=dev)
     else:
         d = torch.empty((rows, N), dtype=torch.bfloat16, device=dev)
-    L = dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, G=G, ue8m0=ue8m0)
+    L = dict(kind=kind, s=s, a=a, qa=qa, sa=sa, ws=ws, d=d, meta=meta, rows=rows, valid=valid, active=active, G=G, ue8m0=ue8m0)
     if ffn:  # the FP8 activation between the GEMMs and the FFN output
         H, I = s["H"], s["I"]
         lead = (s["G"], s["M_max"]) if base == "masked" else (rows,)
@@ -379,7 +384,7 @@ def main():
     kernels = []
     step_flops = 0.0
     for L in layers:
-        f, _ = layer_work(L["kind"], L["s"], L["valid"])
+        f, _ = layer_work(L["kind"], L["s"], L["valid"], L["active"])
         step_flops += f
     def grouped(L, base, a, sa, qb, sb, d):
         u = L["ue8m0"]
@@ -409,19 +414,19 @@ def main():
                  lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
                                                    L["meta"], expected_m=expected_m(L), hq=L["hq"], sfh=L["sh"],
                                                    ue8m0=L["ue8m0"]),
-                 swiglu_work(s_, L["valid"]), True),
+                 swiglu_work(s_, L["valid"], L["active"]), True),
                 ("down N=%d K=%d" % (H, I),
                  lambda c, L=L, base=base: grouped(L, base, L["hq"], L["sh"], *L["ws"][c % len(L["ws"])][2:], L["y"]),
-                 layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"]), True),
+                 layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"], L["active"]), True),
                 # the same gate/up product as a plain GEMM with bf16 output: the cost of the epilogue
                 ("plain gate/up (bf16 out, not in the step) N=%d K=%d" % (2 * I, H),
                  lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2], L["d"]),
-                 layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"]), False),
+                 layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"], L["active"]), False),
             ]
         else:
             timed.append(("gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
                                                                    *L["ws"][c % len(L["ws"])][:2], L["d"]),
-                          layer_work(kind, s_, L["valid"]), True))
+                          layer_work(kind, s_, L["valid"], L["active"]), True))
         for lab, fn, (f, b), in_step in timed:
             gr = capture(torch, lambda fn=fn: [fn(c) for c in range(copies)])
             n = max(1, reps // copies)
