@@ -87,6 +87,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait until at most n groups of P vector-memory loads are outstanding, for a runtime
+// n (clamped to [0, MAXN]): s_waitcnt takes an immediate, so this unrolls to a chain.
+template <int P, int MAXN>
+__device__ __forceinline__ void wait_groups(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<MAXN * P>();
+    else wait_groups<P, MAXN - 1>(n);
+  }
+}
 
 // K split of one 128-byte operand row over the four lane groups g = l >> 4 of an MFMA:
 // group g holds bytes [16g, 16g+16) and [64+16g, 64+16g+16). A and B use the same split,
@@ -389,6 +400,217 @@ inline size_t decode2_need(int bn, int kg, int nkb) {  // bytes of dynamic LDS
   const size_t a = (size_t)nkb * 8192 + (size_t)nkb * 256;  // A block + its scales
   const size_t r = (size_t)kg * 64 * bn * 4;                 // the K-groups' partial tiles
   return a > r ? a : r;
+}
+
+// ---------------------------------------------------------------------------------
+// decode schedule with the activation block resident in LDS and a weight ring
+// ---------------------------------------------------------------------------------
+// For 64-row blocks whose 64 x K activation bytes fit in LDS beside the ring. A workgroup
+// owns 64 rows x BN = 16 * WN * TN columns; its WM x WN waves split them, wave (wm, wn)
+// taking row strips wm*TM .. +TM (TM = 4 / WM) and column strips wn*TN .. +TN:
+//   1. prologue: the activation block ([K block][64 rows][128 B], 16-byte chunks XOR-swizzled
+//      by row), its scales and the weight scales of the (at most two) 128-column blocks the
+//      tile touches go straight into LDS; then the first S-1 K blocks of the weight columns
+//      ([BN rows][128 B], same swizzle) into the ring;
+//   2. per K block: wait for its weights, one barrier, refill the slot the previous K block
+//      freed, TM x TN MFMAs per wave promoted by sa * sb (or, with power-of-two scales, applied
+//      by the matrix unit). Only weights move per K block: a CU keeps S-1 K blocks of them in
+//      flight and reads the activation block once;
+//   3. the bf16 tile goes through LDS and leaves as 16-byte row pieces.
+// The K blocks are summed in order with the same fp32 operations and the same MFMA operand
+// split as the tile kernels, so the results agree with theirs bit for bit.
+inline size_t decode3_need(int bn, int stages, int nkb) {  // bytes of dynamic LDS
+  const size_t ring = (size_t)nkb * 8192 + (size_t)nkb * 256 + (size_t)((8 * nkb + 15) & ~15);
+  const size_t need = ring + (size_t)stages * bn * 128;
+  const size_t tile = (size_t)64 * (2 * bn + 16);  // the epilogue's bf16 tile
+  return need > tile ? need : tile;
+}
+
+template <int WM, int WN, int TN, int S, Layout L, bool kPow2>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_decode3_kernel(KParams p) {
+  static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
+  constexpr int NW = WM * WN, TM = 4 / WM;  // wave (wm, wn): row strips wm*TM.., column strips wn*TN..
+  constexpr int BN = 16 * WN * TN;
+  static_assert(TM * WM == 4, "the wave rows split the 4 row strips");
+  constexpr int PB = BN * 8 / (64 * NW);  // direct loads per wave per K block of weights
+  constexpr int RING = BN * (int)kQ;      // bytes per ring slot
+  constexpr int PITCH = 2 * BN + 16;      // epilogue tile row (the pad spreads LDS banks)
+  static_assert(PB * 64 * NW == BN * 8 && BN <= (int)kQ, "weight ring split, at most two scale blocks");
+  static_assert(S >= 2 && (S - 1) * PB < 64, "ring depth");
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
+  const int nt = (int)(wg % (uint32_t)p.tiles_n);
+  const int mb = (int)((wg / (uint32_t)p.tiles_n) % (uint32_t)p.tiles_m);
+  const int g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  const int64_t m0 = (int64_t)mb * 64;
+  int64_t valid = p.M;
+  if constexpr (L == Layout::Masked) valid = clamp_rows(p.masked_m[g], p.M);
+  if (m0 >= valid) return;  // uniform over the workgroup
+  const int64_t n0 = (int64_t)nt * BN;
+  const int nkb = p.nkb;
+  const int64_t K = p.K;
+  const uint8_t* A = p.a + ((L == Layout::Masked ? (int64_t)g * p.M : 0) + m0) * K;  // this row block
+  const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0) + m0;   // + kb * M + row
+  const uint8_t* B = p.b + ((int64_t)g * p.N + n0) * K;                                // the tile's rows
+  const float* SBg = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
+  uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
+
+  const int t = threadIdx.x, l = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int rows = (int)(valid - m0 < 64 ? valid - m0 : 64);  // rows >= this are clamped
+  const uint32_t base = (uint32_t)(uintptr_t)smem;
+  const uint32_t offSA = (uint32_t)nkb * 8192, offSB = offSA + (uint32_t)nkb * 256;
+  const uint32_t offR = offSB + (uint32_t)((8 * nkb + 15) & ~15);
+  const int64_t b0 = n0 / kQ;  // the tile's first weight-scale block
+
+  // 1. activation block, its scales and the weight scales, then the first weight K blocks;
+  //    loads complete in issue order, so the wait for weight K block 0 covers all of these
+  {
+    const int row = l >> 3;
+    for (int q = w; q < 8 * nkb; q += NW) {  // instruction q: K block q/8, rows 8*(q%8) .. +8
+      const int kb = q >> 3, rb = q & 7;
+      const int r = 8 * rb + row;
+      const int rc = r < rows ? r : rows - 1;
+      const uint32_t voff = (uint32_t)((int64_t)rc * K) + (uint32_t)(kb * kQ) + (uint32_t)((((l & 7) ^ (r & 7))) << 4);
+      lds_dma16(voff, A, base + (uint32_t)(kb * 8192 + rb * 1024));
+    }
+    const uint32_t soff = (uint32_t)((l < rows ? l : rows - 1) * 4);
+    for (int kb = w; kb < nkb; kb += NW) lds_dma4(soff, SA + (int64_t)kb * p.M, base + offSA + (uint32_t)(kb * 256));
+    if (w == NW - 1) {
+      const int64_t last = p.N / kQ - 1;
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        const float* src = SBg + (b0 + bi < last ? b0 + bi : last) * nkb;
+        for (int q = 0; q < nkb; q += 64)
+          if (q + l < nkb) lds_dma4((uint32_t)((q + l) * 4), src, base + offSB + (uint32_t)((bi * nkb + q) * 4));
+      }
+    }
+  }
+  uint32_t boff[PB];
+#pragma unroll
+  for (int u = 0; u < PB; ++u) {
+    const int row = (u * NW + w) * 8 + (l >> 3);
+    boff[u] = (uint32_t)(row * K) + (uint32_t)(((l & 7) ^ ((l >> 3) & 7)) << 4);
+  }
+  auto issue = [&](int kb) {
+    const uint32_t sb = base + offR + (uint32_t)((kb % S) * RING);
+    const uint8_t* bb = B + (int64_t)kb * kQ;
+#pragma unroll
+    for (int u = 0; u < PB; ++u) lds_dma16(boff[u], bb, sb + (uint32_t)((u * NW + w) * 1024));
+  };
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q)
+    if (q < nkb) issue(q);
+
+  // 2. the K loop. The activation fragments and scales of K block kb+1 are read from LDS
+  //    (resident, no wait needed) while K block kb's MFMAs run; every operand read of a K
+  //    block is issued before its first MFMA.
+  const int fr = l & 15, g4 = l >> 4;
+  const uint32_t sw0 = (uint32_t)((g4 ^ (fr & 7)) << 4), sw1 = (uint32_t)(((g4 + 4) ^ (fr & 7)) << 4);
+  const int wm = w % WM, wn = w / WM;
+  int sbi[TN];  // weight-scale block of each strip, relative to b0
+#pragma unroll
+  for (int j = 0; j < TN; ++j) sbi[j] = (int)((n0 + 16 * (wn * TN + j)) / kQ - b0);
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // activation operands of one K block: fragments of the wave's TM row strips and, per lane,
+  // the scales of its 4 output rows in each strip (fp32) or the E8M0 scale of its fragment row
+  auto read_a = [&](v8i (&af)[TM], float4 (&s4)[TM], int kb) {
+    const uint8_t* ak = smem + kb * 8192 + (wm * TM * 16 + fr) * 128;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      af[i] = cat8(*reinterpret_cast<const v4i*>(ak + i * 2048 + sw0), *reinterpret_cast<const v4i*>(ak + i * 2048 + sw1));
+    if constexpr (kPow2) {
+      const float* ek = reinterpret_cast<const float*>(smem + offSA + kb * 256) + wm * TM * 16 + fr;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) s4[i].x = ek[16 * i];
+    } else {
+      const float* sk = reinterpret_cast<const float*>(smem + offSA + kb * 256) + wm * TM * 16 + 4 * g4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) s4[i] = *reinterpret_cast<const float4*>(sk + 16 * i);
+    }
+  };
+  // one K block: wait for its weights, refill the ring, read its weight fragments and the
+  // next K block's activation operands (into the other buffer; past the end a harmless
+  // re-read), then the MFMAs on this K block's activation operands
+  auto step = [&](int kb, const v8i (&afc)[TM], const float4 (&s4c)[TM], v8i (&afn)[TM], float4 (&s4n)[TM]) {
+    if (kb > 0) {
+      wait_groups<PB, S - 2>(nkb - 1 - kb);  // K blocks kb .. min(kb+S-2, nkb-1) are in flight
+      lds_barrier();
+    }
+    if (kb + S - 1 < nkb) issue(kb + S - 1);  // into the slot K block kb-1 used
+    const uint8_t* ring = smem + offR + (kb % S) * RING;
+    v8i bf[TN];
+    float sb[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const uint8_t* bp = ring + (16 * (wn * TN + j) + fr) * (int)kQ;
+      bf[j] = cat8(*reinterpret_cast<const v4i*>(bp + sw0), *reinterpret_cast<const v4i*>(bp + sw1));
+      sb[j] = reinterpret_cast<const float*>(smem + offSB)[sbi[j] * nkb + kb];
+    }
+    read_a(afn, s4n, kb + 1 < nkb ? kb + 1 : kb);
+    if constexpr (kPow2) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = mfma_f8_16x16x128_scaled(afc[i], bf[j], acc[i][j], (int)(__float_as_uint(s4c[i].x) >> 23),
+                                               (int)(__float_as_uint(sb[j]) >> 23));
+    } else {
+      // every product of the K block in its own registers, so the MFMAs issue back to back
+      // and the promotions of the first ones overlap the last ones (one shared result
+      // register would serialise MFMA latency and promotion TM x TN times)
+      v4f pp[TM][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) pp[i][j] = mfma_f8_16x16x128(afc[i], bf[j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j][0] = fmaf(pp[i][j][0], s4c[i].x * sb[j], acc[i][j][0]);
+          acc[i][j][1] = fmaf(pp[i][j][1], s4c[i].y * sb[j], acc[i][j][1]);
+          acc[i][j][2] = fmaf(pp[i][j][2], s4c[i].z * sb[j], acc[i][j][2]);
+          acc[i][j][3] = fmaf(pp[i][j][3], s4c[i].w * sb[j], acc[i][j][3]);
+        }
+    }
+  };
+  v8i af0[TM], af1[TM];
+  float4 s40[TM], s41[TM];
+  if (nkb > 0) {
+    wait_groups<PB, S - 2>(nkb - 1);  // K block 0's weights, and with them all of the prologue
+    lds_barrier();
+    read_a(af0, s40, 0);
+  }
+  for (int kb = 0; kb < nkb; kb += 2) {  // two K blocks per trip: the operand buffers alternate
+    step(kb, af0, s40, af1, s41);
+    if (kb + 1 < nkb) step(kb + 1, af1, s41, af0, s40);
+  }
+
+  // 3. epilogue: bf16 tile [64][PITCH] in LDS over the activation block, then 16-byte pieces
+  //    of the valid rows
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring and the activation block
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<uint16_t*>(smem + (16 * (wm * TM + i) + 4 * g4 + r) * PITCH + (16 * (wn * TN + j) + fr) * 2) =
+            (uint16_t)bf16_rne(acc[i][j][r]);
+  __syncthreads();
+  constexpr int PPR = BN / 8;  // 16-byte pieces per row
+  for (int e = t; e < 64 * PPR; e += 64 * NW) {
+    const int row = e / PPR, c = e - row * PPR;
+    if (row < rows)
+      *reinterpret_cast<uint4*>(D + (m0 + row) * p.N + n0 + c * 8) = *reinterpret_cast<const uint4*>(smem + row * PITCH + c * 16);
+  }
 }
 
 
@@ -1273,13 +1495,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     if (l < SROWS) lds_dma4(soff, SA + (int64_t)kb * p.M, sbase + (uint32_t)((BM + BN) * kQ + w * SROWS * 4));
   };
 
-  // the tile's weight scales for every K block, through LDS: the loop below must issue no
-  // vector-memory load besides the direct-to-LDS ones (its vmcnt waits count only those)
-  for (int i = t; i < NB * nkb; i += 64 * NW) {
-    const int bi = i / nkb, kb = i % nkb;
-    sSB[bi][kb] = SB[(b_row(bi * (int)kQ) / kQ) * nkb + kb];
+  // the tile's weight scales for every K block, straight into LDS by wave 0 ahead of the
+  // first stage (loads complete in issue order, so the first stage's wait covers them and
+  // the barrier after it publishes them); the loop below issues no other vector-memory
+  // loads (its vmcnt waits count the direct-to-LDS ones only)
+  if (w == 0) {
+    const uint32_t sb_lds = (uint32_t)(uintptr_t)&sSB[0][0];
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      const float* src = SB + (b_row(bi * (int)kQ) / kQ) * nkb;
+      for (int q = 0; q < nkb; q += 64)
+        if (q + l < nkb) lds_dma4((uint32_t)((q + l) * 4), src, sb_lds + (uint32_t)((bi * kMaxKb3 + q) * 4));
+    }
   }
-  __syncthreads();
 
   v4f acc[TM][TN];
 #pragma unroll
@@ -1375,11 +1603,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
       tt[c] = factor(s4[c], sb);
     }
     // every read of stage st is issued; wait for the next stage, then recycle stage st
+    // (stages kb+1 .. min(kb+STAGES-1, nkb-1) are in flight; the last ones issue nothing)
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    wait_groups<PER_STAGE, STAGES - 2>(nkb - 2 - kb);
     lds_barrier();
-    issue(min(kb + STAGES, nkb - 1), st);  // past the end: a harmless reload
-    read_a(a0, s0, sn, 0);
+    if (kb + STAGES < nkb) issue(kb + STAGES, st);
+    read_a(a0, s0, sn, 0);  // after the last K block: unused reads of a stale stage
     // last strip (odd slot): B fragment j is reloaded from stage sn right after the MFMA
     // that last reads it
 #pragma unroll
@@ -1423,9 +1652,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
           acc[i][j] = mfma_f8_16x16x128_scaled(af[c], bf[j], acc[i][j], ea[c], eb);
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    wait_groups<PER_STAGE, STAGES - 2>(nkb - 2 - kb);
     lds_barrier();
-    issue(min(kb + STAGES, nkb - 1), st);  // past the end: a harmless reload
+    if (kb + STAGES < nkb) issue(kb + STAGES, st);
     read_a2(a0, e0, sn, 0);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -1441,8 +1670,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
 
   // prologue: the first STAGES K blocks in flight; wait for K block 0
 #pragma unroll
-  for (int q = 0; q < STAGES; ++q) issue(min(q, nkb - 1), q);
-  wait_vmcnt<(STAGES - 1) * PER_STAGE>();
+  for (int q = 0; q < STAGES; ++q)
+    if (q < nkb) issue(q, q);
+  wait_groups<PER_STAGE, STAGES - 1>((nkb < STAGES ? nkb : STAGES) - 1);
   lds_barrier();
   v8i bf[TN], a0;
   read_b(bf, 0);
@@ -1465,7 +1695,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     }
     promote(1, TM - 1);  // the last strip (odd slot)
   }
-  wait_vmcnt<0>();     // drain the tail reloads before leaving
+  wait_vmcnt<0>();     // nothing is in flight by now; kept as a guard before the epilogue
 
   if constexpr (kSwiglu) {
     swiglu_epilogue<BM, WM, WN, TM, TN, L, kPow2>(p, acc, smem, g, tn, m0, valid, act);
@@ -1653,6 +1883,68 @@ hipError_t run_decode2(KParams kp, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WM, int WN, int TN, int S, Layout L>
+hipError_t run_decode3(KParams kp, hipStream_t s) {
+  constexpr int BN = 16 * WN * TN, NW = WM * WN;
+  const size_t lds = decode3_need(BN, S, kp.nkb);
+  if (kp.N % BN != 0 || lds > kLdsBytes || 64 * kp.K >= ((int64_t)1 << 31) || kp.N * 64 >= ((int64_t)1 << 31))
+    return hipErrorNotSupported;
+  kp.tiles_n = (int)(kp.N / BN);
+  kp.tiles_m = (int)((kp.M + 63) / 64);
+  const int64_t nwg = (int64_t)kp.G * kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  if (kp.pow2) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode3_kernel<WM, WN, TN, S, L, true>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    gemm_decode3_kernel<WM, WN, TN, S, L, true><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
+  } else {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode3_kernel<WM, WN, TN, S, L, false>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    gemm_decode3_kernel<WM, WN, TN, S, L, false><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
+  }
+  return hipGetLastError();
+}
+
+// Instantiated configurations of the activation-resident decode schedule: (wave rows, wave
+// columns, column strips per wave, ring slots). DG_DECODE3="wm,wn,strips,slots" forces one
+// (tuning, tests).
+#define DG_DECODE3_CONFIGS(X) \
+  X(2, 2, 3, 4) X(2, 2, 3, 5) X(1, 6, 1, 4) X(1, 6, 1, 5) X(2, 3, 2, 4) X(4, 1, 6, 4) X(1, 8, 1, 3) X(2, 4, 1, 3)
+
+template <Layout L>
+hipError_t run_decode3_cfg(int wm, int wn, int tn, int st, const KParams& kp, hipStream_t s) {
+#define DG_X(a, b, c, d) \
+  if (wm == a && wn == b && tn == c && st == d) return run_decode3<a, b, c, d, L>(kp, s);
+  DG_DECODE3_CONFIGS(DG_X)
+#undef DG_X
+  return hipErrorNotSupported;
+}
+
+// The activation-resident decode schedule when it applies: the configuration from
+// DG_DECODE3, else 96-column tiles (2 x 2 waves, 4 ring slots) when N splits into enough of
+// them to give every CU a workgroup. false leaves the choice to the caller.
+template <Layout L>
+bool try_decode3(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
+  static thread_local char name[48];
+  int wm = 2, wn = 2, tn = 3, st = 4;
+  const char* env = getenv("DG_DECODE3");
+  if (env && sscanf(env, "%d,%d,%d,%d", &wm, &wn, &tn, &st) == 4) {
+  } else {
+    const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
+    if (kp.N % 96 != 0 || rowblocks * (kp.N / 96) < 240) return false;
+  }
+  const hipError_t e = run_decode3_cfg<L>(wm, wn, tn, st, kp, s);
+  if (e == hipErrorNotSupported) return false;
+  *err = e;
+  snprintf(name, sizeof name, "decode3_%dx%d_tn%d_s%d", wm, wn, tn, st);
+  if (chosen) *chosen = name;
+  return true;
+}
+
 // Instantiated configurations of the LDS decode schedule, in order of preference:
 // (columns per workgroup, K-groups, K blocks per wave, waves). Wider workgroups read the
 // activation block fewer times; the first one that covers K, divides N, fits LDS and
@@ -1710,6 +2002,7 @@ hipError_t run_decode_auto(const KParams& kp, hipStream_t s, const char** chosen
   const char* which = getenv("DG_DECODE");  // tuning: "v1" keeps the register-fed schedule
   if (!(which && strcmp(which, "v1") == 0)) {
     hipError_t e = hipSuccess;
+    if (!getenv("DG_DECODE2") && try_decode3<L>(kp, s, chosen, &e)) return e;
     if (try_decode2<L>(kp, s, chosen, &e)) return e;
   }
   if (getenv("DG_DECODE_LDS")) {  // tuning: the LDS-resident variant
@@ -1762,15 +2055,18 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G; kp.pow2 = p.pow2;
 
   if (sched == Schedule::Auto) {
-    // dense M <= 64: 64x128 direct-load tiles when they make enough workgroups to cover the
-    // chip (measured 5% faster than the decode schedule on 64x24576x1536), else the decode
-    // schedule
-    if (p.layout == Layout::Dense)
-      sched = p.M <= 64 ? (p.N % 128 == 0 && p.N / 128 >= 160 && !getenv("DG_DECODE") &&
+    // dense M <= 64: the decode schedules, which take the activation-resident one (96-column
+    // tiles) when N gives every CU a tile; otherwise 64x128 direct-load tiles when they make
+    // enough workgroups to cover the chip (measured 5% faster than the LDS decode schedule on
+    // 64x24576x1536), else the LDS decode schedule
+    if (p.layout == Layout::Dense) {
+      const bool d3 = p.N % 96 == 0 && p.N / 96 >= 240 && decode3_need(96, 4, kp.nkb) <= kLdsBytes;
+      sched = p.M <= 64 ? (!d3 && p.N % 128 == 0 && p.N / 128 >= 160 && !getenv("DG_DECODE") &&
                                    !getenv("DG_DECODE2")
                                ? Schedule::Tile64
                                : Schedule::Decode)
                         : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
+    }
     else if (p.layout == Layout::Masked)
       // the direct-load tiles at every count: at decode-sized counts they stream the weights
       // at 5-6.4 TB/s where the decode schedule (one 64-row block per workgroup, weights
@@ -1810,6 +2106,11 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       if (is("t3_128x256")) {
         pick("tile3_128x256");
         const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Dense>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
+      if (is("d3_96")) {  // the activation-resident decode kernel, where it fits
+        pick("decode3_2x2_tn3_s4");
+        const hipError_t e = run_decode3<2, 2, 3, 4, Layout::Dense>(kp, stream);
         if (e != hipErrorNotSupported) return e;
       }
       if (sched == Schedule::Tile64 || is("t3_64x128")) {

@@ -44,7 +44,7 @@ def test_shape_sweep(dg, sched, M, N, K):
 
 
 @pytest.mark.parametrize("N,K", [(7168, 2048), (24576, 1536)])
-def test_decode_full_size(dg, N, K):
+def test_decode_full_size(dg, monkeypatch, N, K):
     # the decode configurations, M = 64, in full against the whole oracle result
     say("dense decode full M=64 N=%d K=%d" % (N, K))
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, 64, N, K, seed=0)
@@ -54,6 +54,15 @@ def test_decode_full_size(dg, N, K):
     for sched in ("decode", "tile128", "tile256"):
         d2 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES[sched])
         assert_close(bf16_values(d2), R, "decode %dx%d %s" % (N, K, sched))
+    # the activation-resident decode kernel and the 64x128 tile kernel sum the K blocks in
+    # the same order with the same operations: bit for bit the same output
+    monkeypatch.setenv("DG_TILE", "t3_64x128")
+    d3 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
+    monkeypatch.setenv("DG_TILE", "d3_96")
+    d4 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
+    monkeypatch.delenv("DG_TILE")
+    assert_close(bf16_values(d3), R, "decode %dx%d tile3 64x128" % (N, K))
+    assert torch.equal(d3.view(torch.int16), d4.view(torch.int16))
 
 
 @pytest.mark.slow
@@ -155,7 +164,7 @@ def test_empty_problems_launch_nothing(dg):
 
 # every tile kernel, forced through DG_TILE (None = the automatic choice); they all sum the
 # K blocks in the same order with the same fp32 operations, so they must agree bit for bit
-TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "t3_64x128"]
+TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "t3_64x128", "d3_96"]
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 1280), (512, 256, 2304), (77, 768, 384), (1000, 640, 640),
@@ -179,11 +188,16 @@ def test_tile_kernels_parity_and_agreement(dg, monkeypatch, M, N, K):
             assert torch.equal(bits, ref), "tile kernel %s differs from the automatic choice" % v
 
 
-# decode schedules, forced one by one: the register-fed one (DG_DECODE=v1) and the LDS ones
-# (DG_DECODE2="bn,kg,kpw,waves"); each against the oracle, on full and partial 64-row blocks
+# decode schedules, forced one by one: the register-fed one (DG_DECODE=v1), the LDS ones
+# (DG_DECODE2="bn,kg,kpw,waves") and the activation-resident ones (DG_DECODE3="wave rows,wave columns,strips,
+# slots"; where the activations do not fit beside the ring they fall back to the LDS ones);
+# each against the oracle, on full and partial 64-row blocks
 DECODE_VARIANTS = [("DG_DECODE", "v1"), ("DG_DECODE2", "96,4,3,8"), ("DG_DECODE2", "96,1,12,6"),
                    ("DG_DECODE2", "96,2,6,6"), ("DG_DECODE2", "32,8,2,8"), ("DG_DECODE2", "32,2,8,4"),
-                   ("DG_DECODE2", "32,1,16,2"), ("DG_DECODE2", "16,8,3,8"), ("DG_DECODE2", "128,4,3,8")]
+                   ("DG_DECODE2", "32,1,16,2"), ("DG_DECODE2", "16,8,3,8"), ("DG_DECODE2", "128,4,3,8"),
+                   ("DG_DECODE3", "2,2,3,4"), ("DG_DECODE3", "2,2,3,5"), ("DG_DECODE3", "1,6,1,4"),
+                   ("DG_DECODE3", "2,3,2,4"), ("DG_DECODE3", "4,1,6,4"), ("DG_DECODE3", "1,8,1,3"),
+                   ("DG_DECODE3", "2,4,1,3"), ("DG_DECODE3", "1,6,1,5")]
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 1536, 1536), (37, 768, 2048), (1, 384, 1152), (130, 768, 1024)])
@@ -191,8 +205,8 @@ def test_decode_variants(dg, monkeypatch, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 11)
     R = oracle.gemm(oqa, osa, oqb, osb)
     for var, val in DECODE_VARIANTS:
-        monkeypatch.delenv("DG_DECODE", raising=False)
-        monkeypatch.delenv("DG_DECODE2", raising=False)
+        for v in ("DG_DECODE", "DG_DECODE2", "DG_DECODE3"):
+            monkeypatch.delenv(v, raising=False)
         monkeypatch.setenv(var, val)
         say("decode %s=%s M=%d N=%d K=%d" % (var, val, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["decode"])

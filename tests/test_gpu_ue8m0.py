@@ -62,18 +62,23 @@ def test_dense_ue8m0_tile_kernels(dg, monkeypatch, M, N, K):
         assert_close(bf16_values(d), R, "ue8m0 tile %s" % v)
 
 
-DECODE = [None, "96,4,3,8", "96,1,12,6", "32,8,2,8", "32,1,16,2", "16,8,3,8"]
+# (variable, value): the LDS decode schedule's configurations and the activation-resident
+# ones (which fall back to the former where the activations do not fit beside the ring)
+DECODE = [(None, None), ("DG_DECODE2", "96,4,3,8"), ("DG_DECODE2", "96,1,12,6"), ("DG_DECODE2", "32,8,2,8"),
+          ("DG_DECODE2", "32,1,16,2"), ("DG_DECODE2", "16,8,3,8"), ("DG_DECODE3", "2,2,3,4"),
+          ("DG_DECODE3", "1,6,1,4"), ("DG_DECODE3", "2,3,2,4"), ("DG_DECODE3", "4,1,6,4"), ("DG_DECODE3", "1,8,1,3")]
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 1536, 1536), (37, 768, 2048), (130, 384, 1152)])
 def test_dense_ue8m0_decode(dg, monkeypatch, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 2, ue8m0=True)
     R = oracle.gemm(oqa, osa, oqb, osb)
-    for v in DECODE:
+    for var, v in DECODE:
         monkeypatch.delenv("DG_DECODE2", raising=False)
-        if v:
-            monkeypatch.setenv("DG_DECODE2", v)
-        say("dense ue8m0 decode %s M=%d N=%d K=%d" % (v, M, N, K))
+        monkeypatch.delenv("DG_DECODE3", raising=False)
+        if var:
+            monkeypatch.setenv(var, v)
+        say("dense ue8m0 decode %s=%s M=%d N=%d K=%d" % (var, v, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=1, ue8m0=True)
         assert_close(bf16_values(d), R, "ue8m0 decode %s" % v)
     d = dg.gemm_fp8_nt(qa, sa, qb, sb, ue8m0=True)  # automatic choice
