@@ -1925,12 +1925,14 @@ hipError_t run_decode3_cfg(int wm, int wn, int tn, int st, const KParams& kp, hi
 }
 
 // The activation-resident decode schedule when it applies: the configuration from
-// DG_DECODE3, else 96-column tiles (2 x 2 waves, 4 ring slots) when N splits into enough of
-// them to give every CU a workgroup. false leaves the choice to the caller.
+// DG_DECODE3, else 96-column tiles (2 x 3 waves of 2 x 2 MFMA tiles, 4 ring slots: measured
+// fastest of the instantiated ones on 64x24576x1536, 5% ahead of the 64x128 tile kernel) when
+// N splits into enough of them to give every CU a workgroup. false leaves the choice to the
+// caller.
 template <Layout L>
 bool try_decode3(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
   static thread_local char name[48];
-  int wm = 2, wn = 2, tn = 3, st = 4;
+  int wm = 2, wn = 3, tn = 2, st = 4;
   const char* env = getenv("DG_DECODE3");
   if (env && sscanf(env, "%d,%d,%d,%d", &wm, &wn, &tn, &st) == 4) {
   } else {
@@ -2109,8 +2111,8 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         if (e != hipErrorNotSupported) return e;
       }
       if (is("d3_96")) {  // the activation-resident decode kernel, where it fits
-        pick("decode3_2x2_tn3_s4");
-        const hipError_t e = run_decode3<2, 2, 3, 4, Layout::Dense>(kp, stream);
+        pick("decode3_2x3_tn2_s4");
+        const hipError_t e = run_decode3<2, 3, 2, 4, Layout::Dense>(kp, stream);
         if (e != hipErrorNotSupported) return e;
       }
       if (sched == Schedule::Tile64 || is("t3_64x128")) {
