@@ -133,14 +133,16 @@ def test_output_guard_bands(dg):
 def test_zero_and_extreme_scales(dg):
     M, N, K = 64, 256, 512
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=8)
-    sa2 = sa.clone()         # K-block-major: sa2[kb, m]
-    sa2[1, :] = 0.0          # a K block switched off
-    sa2[:, 3] = 0.0          # a whole row of zero scales
-    sa2[:, 5] *= 1e-20       # tiny scales
-    sb2 = sb.clone()
-    sb2[1, :] *= 1e15        # large weight scales on the second column block
-    osa2 = np.ascontiguousarray(sa2.cpu().numpy().T)
-    osb2 = sb2.cpu().numpy()
+    # the scales are edited on the oracle's side ([M, K/128] and [N/128, K/128]) and the GPU
+    # gets copies of them (its activation scales K-block-major)
+    osa2 = osa.copy()
+    osa2[:, 1] = 0.0                                   # a K block switched off
+    osa2[3, :] = 0.0                                   # a whole row of zero scales
+    osa2[5, :] = osa2[5, :] * np.float32(1e-20)        # tiny scales
+    osb2 = osb.copy()
+    osb2[1, :] = osb2[1, :] * np.float32(1e15)         # large weight scales on the second column block
+    sa2 = torch.from_numpy(np.ascontiguousarray(osa2.T)).to("cuda:0")
+    sb2 = torch.from_numpy(np.ascontiguousarray(osb2)).to("cuda:0")
     R = oracle.gemm(oqa, osa2, oqb, osb2)
     for sched in SCHEDULES.values():
         say("dense zero/extreme scales schedule %d" % sched)

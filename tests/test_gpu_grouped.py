@@ -137,9 +137,11 @@ def test_masked_parity_and_sentinels(dg, sched):
     mm = [0, 1, 63, 64, 200, 130]
     (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 11, mm)
     # invalid A rows hold the NaN code: they must not leak into valid rows
+    # (the oracle's copy gets the same codes, planted in its own cast, not read back)
+    oqa_nan = oqa.copy()
     for g in range(G):
         qa[g, mm[g]:] = 0x7F
-    oqa_nan = qa.cpu().numpy()
+        oqa_nan[g, mm[g]:] = 0x7F
     d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("masked %s G=%d M_max=%d N=%d K=%d" % (sched, G, M_max, N, K))
     dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, expected_m=48 if sched == "auto" else 0, d=d,
@@ -169,6 +171,30 @@ def test_masked_tile_kernels(dg, monkeypatch, variant):
     d2 = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d2, schedule=MASKED_SCHEDULES["tile256"])
     assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", ["2,3,2,4", "1,6,1,4", "2,2,3,5", "1,8,1,3"])
+def test_masked_activation_resident_decode(dg, monkeypatch, cfg):
+    # the activation-resident decode kernel on the masked layout, forced through DG_DECODE3
+    # (decode schedule): empty, partial, full and multi-row-block groups, NaN codes in the
+    # invalid activation rows, sentinels beyond the valid rows
+    G, M_max, N, K = 5, 130, 384, 1024
+    mm = [0, 5, 64, 130, 100]
+    (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 31, mm)
+    # (the oracle's copy gets the same codes, planted in its own cast, not read back)
+    oqa_nan = oqa.copy()
+    for g in range(G):
+        qa[g, mm[g]:] = 0x7F
+        oqa_nan[g, mm[g]:] = 0x7F
+    monkeypatch.setenv("DG_DECODE3", cfg)
+    d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    say("masked decode3 %s G=%d M_max=%d N=%d K=%d" % (cfg, G, M_max, N, K))
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["decode"])
+    R = oracle.grouped_masked(oqa_nan, osa, oqb, osb, omm)
+    valid = np.isfinite(R)
+    assert_close(bf16_values(d), R, "masked decode3 %s" % cfg, mask=valid)
+    bits = d.view(torch.int16).cpu().numpy()
+    assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
 
 
 def test_masked_clamps_out_of_range_counts(dg):

@@ -116,7 +116,10 @@ def test_contiguous_ue8m0(dg, monkeypatch):
         assert_close(bf16_values(d), R, "contiguous ue8m0 %s" % v, mask=valid)
 
 
-@pytest.mark.parametrize("sched,tile", [(1, None), (3, None), (3, "t3_128x256"), (2, None)])
+# tile: a tile kernel forced through DG_TILE, or "d3:..." the activation-resident decode
+# kernel forced through DG_DECODE3 (decode schedule)
+@pytest.mark.parametrize("sched,tile", [(1, None), (3, None), (3, "t3_128x256"), (2, None), (1, "d3:1,8,1,3"),
+                                        (1, "d3:2,4,1,3")])
 def test_masked_ue8m0_parity_and_sentinels(dg, monkeypatch, sched, tile):
     G, M_max, N, K = 5, 300, 512, 768
     mm = np.array([0, 17, 128, 257, 300], np.int32)
@@ -126,7 +129,9 @@ def test_masked_ue8m0_parity_and_sentinels(dg, monkeypatch, sched, tile):
     oqa, osa = oracle.cast_per_token(a.reshape(-1, K), pow2=True)
     oqb, osb = oracle.cast_per_block(b, pow2=True)
     R = oracle.grouped_masked(oqa.reshape(G, M_max, K), osa.reshape(G, M_max, K // 128), oqb, osb, mm)
-    if tile:
+    if tile and tile.startswith("d3:"):
+        monkeypatch.setenv("DG_DECODE3", tile[3:])
+    elif tile:
         monkeypatch.setenv("DG_TILE", tile)
     d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("masked ue8m0 schedule %d tile %s" % (sched, tile))
