@@ -32,7 +32,8 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 7168, 2048), (64, 1024, 1536), (300, 512, 1024)])
+# the shapes take the LDS decode kernel, the activation-resident decode kernel, and the tiles
+@pytest.mark.parametrize("M,N,K", [(64, 7168, 2048), (64, 1024, 1536), (64, 24576, 1536), (300, 512, 1024)])
 def test_cast_and_gemm_graph_replays_match_eager(dg, M, N, K):
     dev = torch.device("cuda:0")
     a32, b32 = synth.dense_inputs(M, N, K, seed=3)
