@@ -230,7 +230,8 @@ def compare(y, R, mask=None) -> dict:
       per element  |y - R| <= 2^-7 |R| + 1e-3 rms_S(R)
       global       1 - 2 sum(yR) / sum(y^2 + R^2) <= 1e-5   (0 when the denominator is 0)
     Returns a dict with 'ok', 'worst_excess', 'n_bad', 'sim'."""
-    y = np.asarray(y, np.float64)
+    with np.errstate(invalid="ignore"):  # unwritten rows may hold signalling-NaN patterns
+        y = np.asarray(y, np.float64)
     R = np.asarray(R, np.float64)
     if mask is None:
         mask = np.isfinite(R)
