@@ -63,6 +63,9 @@ __device__ __forceinline__ void lds_barrier() {
 // bytes [16i, 16i+16) (or [4i, 4i+4)) after the LDS base held in M0). They are issued from
 // inline assembly: they write only LDS and have no output registers; an address is a
 // wave-uniform 64-bit base plus a per-lane 32-bit offset. Waits for them are explicit.
+// M0 is listed as clobbered (the compiler warns that it cannot preserve a reserved register
+// across the statement): in these kernels nothing else uses M0, every M0 write in the
+// generated code being one of these, so there is nothing to preserve.
 // Wave-uniform values in scalar registers; a no-op for values already there. The operands
 // below must be uniform, and the compiler cannot always prove that they are.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {

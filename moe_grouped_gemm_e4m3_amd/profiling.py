@@ -34,12 +34,42 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 COPY_BYTES = 256 * 2 ** 20  # the reference copy: 64 Mi float32 elements
 
 
-def source_hash() -> str:
-    """Hash of the GEMM kernel sources; counter figures are valid only for this source."""
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed (string and
+    character literals kept as they are), so that editing a comment keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def source_hash(texts=None) -> str:
+    """Hash of the GEMM kernel sources' code (comments and layout excluded); counter figures
+    are valid only for this code. `texts` (gemm.hip, dg_device.h contents) defaults to the
+    files in csrc/."""
+    if texts is None:
+        texts = []
+        for f in ("gemm.hip", "dg_device.h"):
+            with open(os.path.join(_PKG, "csrc", f), encoding="utf-8") as fh:
+                texts.append(fh.read())
     h = hashlib.sha256()
-    for f in ("gemm.hip", "dg_device.h"):
-        with open(os.path.join(_PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for t in texts:
+        h.update(_code_only(t).encode())
     return h.hexdigest()[:16]
 
 
