@@ -166,7 +166,7 @@ def test_empty_problems_launch_nothing(dg):
 
 # every tile kernel, forced through DG_TILE (None = the automatic choice); they all sum the
 # K blocks in the same order with the same fp32 operations, so they must agree bit for bit
-TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "t3_64x128", "d3_96"]
+TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "t3_64x128", "d3_96", "t3_256x256b"]
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 1280), (512, 256, 2304), (77, 768, 384), (1000, 640, 640),

@@ -153,7 +153,7 @@ def test_masked_parity_and_sentinels(dg, sched):
     assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
 
 
-@pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128"])
+@pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128", "t3_256x256b"])
 def test_masked_tile_kernels(dg, monkeypatch, variant):
     G, M_max, N, K = 5, 300, 512, 768
     mm = [0, 17, 128, 257, 300]

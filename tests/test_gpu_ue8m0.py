@@ -45,7 +45,7 @@ def test_cast_per_block_ue8m0_bit_exact(dg):
     assert_same_bits(s, so, "s")
 
 
-TILES = [None, "t3_256x128", "t3_128x256", "t2_256x128", "t2_128x128"]
+TILES = [None, "t3_256x128", "t3_128x256", "t2_256x128", "t2_128x128", "t3_256x256b"]
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 2304), (300, 768, 1280), (77, 256, 384), (256, 256, 128)])
