@@ -1402,11 +1402,11 @@ __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM]
   }
 }
 
-// kSplit (two stages only): a stage's weight rows are dead once every wave holds their
-// fragments, at the start of the K block, while its activation rows are read strip by strip
-// until the middle of it. The weights of K block kb+2 are then issued at the start of K block
-// kb and its activations after the middle barrier, so that up to one and a half K blocks of
-// loads are in flight instead of one, for a second barrier per K block.
+// kSplit: a stage's weight rows are dead once every wave holds their fragments, at the start
+// of the K block, while its activation rows are read strip by strip until the middle of it.
+// The weights of K block kb+STAGES are then issued at the start of K block kb and its
+// activations after the middle barrier, so that half a K block more of loads is in flight,
+// for a second barrier per K block.
 template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2, bool kSwiglu = false, bool kSplit = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   constexpr int NW = WM * WN;
@@ -1424,7 +1424,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
   static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 1) * PER_STAGE < 64, "LDS ring depth");
-  static_assert(!kSplit || STAGES == 2, "split issue: two stages");
+  static_assert(!kSplit || (STAGES - 2) * PER_STAGE + BDMA < 64, "split issue: loads in flight");
   static_assert(STAGES * STAGE_BYTES + NB * kMaxKb3 * 4 <= 160 * 1024, "LDS");
   static_assert(!kSwiglu || (BN == 2 * (int)kQ && TM % 2 == 0), "SwiGLU tile: 128 gate + 128 up rows");
   static_assert(!kSwiglu || (32 * (BM + 4) * 4 + BM * 8 + BM * (int)kQ <= STAGES * STAGE_BYTES &&
@@ -1519,21 +1519,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
     for (int u = 0; u < BDMA; ++u) lds_dma16(boff[u], bb, sbase + (uint32_t)(BM * kQ + (u * NW + w) * 1024));
   };
   // start of K block kb (split issue): every wave holds its weight fragments (read at the end
-  // of the previous K block), so its stage's weight rows take those of K block kb+2
+  // of the previous K block), so its stage's weight rows take those of K block kb+STAGES
   auto split_start = [&](int kb, int st) {
     if constexpr (kSplit) {
       lds_barrier();
-      if (kb + 2 < nkb) issue_b(kb + 2, st);
+      if (kb + STAGES < nkb) issue_b(kb + STAGES, st);
     }
   };
-  // middle of K block kb: wait for K block kb+1 (with the split issue only K block kb+2's
-  // weights may stay in flight), one barrier, refill stage st
+  // middle of K block kb: wait for K block kb+1, one barrier, refill stage st. Loads issued
+  // after K block kb+1's may stay in flight: whole stages kb+2 .. kb+STAGES-1 and, with the
+  // split issue, the weights of K block kb+STAGES
   auto refill = [&](int kb, int st) {
     if constexpr (kSplit) {
-      if (kb + 2 < nkb) wait_vmcnt<BDMA>();
-      else wait_vmcnt<0>();
+      if (kb + STAGES < nkb) wait_vmcnt<(STAGES - 2) * PER_STAGE + BDMA>();
+      else wait_groups<PER_STAGE, STAGES - 2>(nkb - 2 - kb);
       lds_barrier();
-      if (kb + 2 < nkb) issue_a(kb + 2, st);
+      if (kb + STAGES < nkb) issue_a(kb + STAGES, st);
     } else {
       wait_groups<PER_STAGE, STAGES - 2>(nkb - 2 - kb);
       lds_barrier();
@@ -2193,6 +2194,11 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         // 128-row tiles when most groups fit in one (each group's weights are then streamed
         // once, with two LDS stages of them in flight); 256-row tiles otherwise
         const bool small = p.M <= 128 || (expected_m > 0 && expected_m <= 64);
+        if (is("t3_128x256b")) {
+          pick("tile3_128x256_split");
+          const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Masked, false, true>(kp, stream);
+          if (e != hipErrorNotSupported) return e;
+        }
         if (is("t3_128x256") || (!force && small)) {
           pick("tile3_128x256");
           const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Masked>(kp, stream);
@@ -2220,6 +2226,11 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       }
       // the three-stage direct-load ring pays off once K is long enough to fill it (measured:
       // 8% faster than the register-staged kernel at K = 2048)
+      if (is("t3_128x256b")) {
+        pick("tile3_128x256_split");
+        const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, false, true>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
       if (is("t3_128x256") || (!force && kp.nkb >= 16)) {
         pick("tile3_128x256");
         const hipError_t e = run_tile3<128, 256, 2, 4, 3, Layout::Contiguous>(kp, stream);
@@ -2247,9 +2258,17 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
   auto pick = [&](const char* name) { if (chosen) *chosen = name; };
   switch (p.layout) {
     case Layout::Contiguous:
+      if (is("t3_128x256b")) {
+        pick("tile3_swiglu_128x256_split");
+        return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true, true>(kp, stream);
+      }
       pick("tile3_swiglu_128x256");
       return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true>(kp, stream);
     case Layout::Masked:
+      if (is("t3_128x256b")) {
+        pick("tile3_swiglu_128x256_split");
+        return run_tile3<128, 256, 2, 4, 3, Layout::Masked, true, true>(kp, stream);
+      }
       if (is("t3_128x256") || (!force && (p.M <= 128 || (expected_m > 0 && expected_m <= 64)))) {
         pick("tile3_swiglu_128x256");
         return run_tile3<128, 256, 2, 4, 3, Layout::Masked, true>(kp, stream);

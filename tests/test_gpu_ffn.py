@@ -161,6 +161,32 @@ def test_ffn_masked(dg, pow2, expected_m):
                 hq.reshape(-1, I), sh.reshape(-1, I // 128), bf16_values(y_d).reshape(-1, H), pow2, "ffn masked")
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "masked"])
+def test_swiglu_split_issue_is_bitwise_the_same(dg, monkeypatch, layout):
+    # the fused gate/up kernel with the split issue (DG_TILE=t3_128x256b) sums the K blocks
+    # exactly as the default 128x256 kernel: same hq bytes, same scales
+    if layout == "contiguous":
+        dev, _, _ = _contiguous_case(dg, 4, 300, 640, 256, 71, False)
+        xq_d, sx_d, w1_d, s1_d, _, _, mi_d = dev
+        run = lambda: dg.gemm_fp8_swiglu(CONTIG, xq_d, sx_d, w1_d, s1_d, mi_d)
+    else:
+        dev, _, _ = _masked_case(dg, 4, 128, 640, 256, 72, False, np.array([0, 128, 77, 5], np.int32))
+        xq_d, sx_d, w1_d, s1_d, _, _, mm_d = dev
+        run = lambda: dg.gemm_fp8_swiglu(MASKED, xq_d, sx_d, w1_d, s1_d, mm_d, expected_m=32)
+    say("swiglu split issue %s" % layout)
+    monkeypatch.delenv("DG_TILE", raising=False)
+    hq1, sh1 = run()
+    monkeypatch.setenv("DG_TILE", "t3_128x256b")
+    hq2, sh2 = run()
+    torch.cuda.synchronize()
+    if layout == "masked":  # rows beyond the counts are not written: compare the valid ones
+        for g, m in enumerate([0, 128, 77, 5]):
+            assert torch.equal(hq1[g, :m], hq2[g, :m]) and torch.equal(sh1[g, :, :m], sh2[g, :, :m])
+    else:
+        rows = torch.nonzero(mi_d >= 0).flatten()
+        assert torch.equal(hq1[rows], hq2[rows]) and torch.equal(sh1[:, rows], sh2[:, rows])
+
+
 def test_swiglu_dense(dg):
     M, H, I = 200, 256, 256
     say("swiglu dense M=%d H=%d I=%d" % (M, H, I))

@@ -43,6 +43,19 @@ def test_shape_sweep(dg, sched, M, N, K):
     assert_close(bf16_values(d), R, "sweep %s %dx%dx%d" % (sched, M, N, K))
 
 
+@pytest.mark.parametrize("sched", list(SCHEDULES))
+def test_long_k_fallbacks(dg, sched):
+    # K = 258 blocks: beyond the 256 K blocks whose weight scales the direct-load tile kernel
+    # keeps in LDS and beyond every LDS decode configuration, so each schedule runs its
+    # fallback kernel; ragged M
+    M, N, K = 70, 256, 258 * 128
+    say("dense long K %s M=%d N=%d K=%d" % (sched, M, N, K))
+    (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=5)
+    d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES[sched])
+    R = oracle.gemm(oqa, osa, oqb, osb)
+    assert_close(bf16_values(d), R, "long K %s" % sched)
+
+
 @pytest.mark.parametrize("N,K", [(7168, 2048), (24576, 1536)])
 def test_decode_full_size(dg, monkeypatch, N, K):
     # the decode configurations, M = 64, in full against the whole oracle result

@@ -61,7 +61,7 @@ def test_contiguous_parity(dg, G, tokens, N, K):
     assert_close(bf16_values(d), R, "contiguous", mask=omi[:, None].repeat(N, 1) >= 0)
 
 
-@pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None])
+@pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None, "t3_128x256b"])
 def test_contiguous_tile_kernels(dg, monkeypatch, variant):
     # long enough K for the automatic choice to take the direct-load ring; each kernel checked
     # against the oracle and against the others bit for bit
@@ -153,7 +153,7 @@ def test_masked_parity_and_sentinels(dg, sched):
     assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
 
 
-@pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128", "t3_256x256b"])
+@pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128", "t3_256x256b", "t3_128x256b"])
 def test_masked_tile_kernels(dg, monkeypatch, variant):
     G, M_max, N, K = 5, 300, 512, 768
     mm = [0, 17, 128, 257, 300]
@@ -195,6 +195,44 @@ def test_masked_activation_resident_decode(dg, monkeypatch, cfg):
     assert_close(bf16_values(d), R, "masked decode3 %s" % cfg, mask=valid)
     bits = d.view(torch.int16).cpu().numpy()
     assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
+
+
+@pytest.mark.parametrize("K", [128, 256, 384])
+def test_masked_split_issue_short_k(dg, K):
+    # the masked 256x256 tiles (weights of K block kb+2 issued at the start of K block kb) with
+    # 1, 2 and 3 K blocks, where the issue and wait steps run into the end of K
+    G, M_max, N = 3, 300, 512
+    mm = [300, 0, 257]
+    (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 40 + K, mm)
+    d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    say("masked split issue G=%d M_max=%d N=%d K=%d" % (G, M_max, N, K))
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["tile256"])
+    R = oracle.grouped_masked(oqa, osa, oqb, osb, omm)
+    valid = np.isfinite(R)
+    assert_close(bf16_values(d), R, "masked split K=%d" % K, mask=valid)
+    assert (d.view(torch.int16).cpu().numpy()[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512])
+def test_split_issue_three_stages_short_k(dg, monkeypatch, K):
+    # the 128x256 tiles with the split issue (three stages: weights of K block kb+3 issued at
+    # the start of K block kb) with 1 to 4 K blocks, on both grouped layouts
+    monkeypatch.setenv("DG_TILE", "t3_128x256b")
+    G, N = 3, 512
+    (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 200, N, K, seed=50 + K)
+    say("contiguous split issue N=%d K=%d" % (N, K))
+    d = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
+    R = oracle.grouped_contiguous(oqa, osa, oqb, osb, omi)
+    assert_close(bf16_values(d), R, "contiguous split K=%d" % K, mask=omi[:, None].repeat(N, 1) >= 0)
+    mm = [100, 0, 128]
+    (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, 128, N, K, 60 + K, mm)
+    d = torch.full((G, 128, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    say("masked split issue (three stages) N=%d K=%d" % (N, K))
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["tile256"])
+    R = oracle.grouped_masked(oqa, osa, oqb, osb, omm)
+    valid = np.isfinite(R)
+    assert_close(bf16_values(d), R, "masked split3 K=%d" % K, mask=valid)
+    assert (d.view(torch.int16).cpu().numpy()[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
 
 
 def test_masked_clamps_out_of_range_counts(dg):
