@@ -187,6 +187,41 @@ def test_swiglu_split_issue_is_bitwise_the_same(dg, monkeypatch, layout):
         assert torch.equal(hq1[rows], hq2[rows]) and torch.equal(sh1[:, rows], sh2[:, rows])
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_ffn_random_shapes(dg, case):
+    # the whole expert FFN on seeded random shapes, both grouped layouts, both scale types,
+    # with the masked layout's expected_m hint picking either gate/up tile
+    r = np.random.default_rng(7000 + case)
+    G, H, I = int(r.integers(1, 6)), 128 * int(r.integers(1, 8)), 128 * int(r.integers(1, 5))
+    pow2 = bool(r.integers(0, 2))
+    if case % 2 == 0:
+        tokens = int(r.integers(1, 700))
+        say("ffn random contiguous case %d: G=%d tokens=%d H=%d I=%d ue8m0=%d" % (case, G, tokens, H, I, pow2))
+        dev, (xq, sx, w1q, s1, w2q, s2, mi), ref = _contiguous_case(dg, G, tokens, H, I, 80 + case, pow2)
+        y_d, hq_d, sh_d = dg.moe_ffn_fp8(CONTIG, *dev, ue8m0=pow2)
+        torch.cuda.synchronize()
+        rows = {e: np.nonzero(mi == e)[0] for e in range(G)}
+        _check_rows(rows, xq, sx, w1q, s1, w2q, s2, ref, hq_d.cpu().numpy(), kmajor(sh_d.cpu().numpy()),
+                    bf16_values(y_d), pow2, "ffn random contiguous %d" % case)
+    else:
+        M_max = int(r.integers(1, 260))
+        mm = r.integers(0, M_max + 1, size=G).astype(np.int32)
+        expected_m = int(r.choice([0, 16, M_max]))
+        say("ffn random masked case %d: G=%d M_max=%d H=%d I=%d counts %s expected_m %d ue8m0=%d"
+            % (case, G, M_max, H, I, mm.tolist(), expected_m, pow2))
+        dev, (xq, sx, w1q, s1, w2q, s2, _), ref = _masked_case(dg, G, M_max, H, I, 90 + case, pow2, mm)
+        y_d = torch.full((G, M_max, H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        _, hq_d, sh_d = dg.moe_ffn_fp8(MASKED, *dev, expected_m=expected_m, y=y_d, ue8m0=pow2)
+        torch.cuda.synchronize()
+        yb = y_d.view(torch.int16).cpu().numpy()
+        for g in range(G):
+            assert np.all(yb[g, mm[g]:] == -1), "y rows beyond masked_m written (group %d)" % g
+        rows = {g: g * M_max + np.arange(mm[g]) for g in range(G)}
+        _check_rows(rows, xq.reshape(-1, H), sx.reshape(-1, H // 128), w1q, s1, w2q, s2, _flat(ref),
+                    hq_d.cpu().numpy().reshape(-1, I), kmajor(sh_d.cpu().numpy()).reshape(-1, I // 128),
+                    bf16_values(y_d).reshape(-1, H), pow2, "ffn random masked %d" % case)
+
+
 def test_swiglu_dense(dg):
     M, H, I = 200, 256, 256
     say("swiglu dense M=%d H=%d I=%d" % (M, H, I))
