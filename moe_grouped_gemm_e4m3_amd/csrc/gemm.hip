@@ -22,6 +22,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "dg_device.h"
 #include "dg_launch.h"
 
@@ -1808,6 +1810,20 @@ hipError_t run_tile(KParams kp, hipStream_t s) {
 
 constexpr size_t kLdsBytes = 163840;  // gfx950 LDS per workgroup
 
+// Lets kernel Fn use the whole LDS as dynamic shared memory. The attribute belongs to the
+// current device, so it is set once per kernel and device (devices 0..63; others every call).
+template <auto Fn>
+hipError_t allow_full_lds() {
+  static std::atomic<bool> done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return hipErrorInvalidDevice;
+  if (dev < 64 && done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)kLdsBytes);
+  if (e == hipSuccess && dev < 64) done[dev].store(true, std::memory_order_release);
+  return e;
+}
+
 template <int TN, int KSPLIT, int NW, int KW>
 constexpr size_t decode_lds_bytes(int64_t K, int nkb) {
   return (size_t)(64 * K) + (size_t)4 * 64 * nkb + (size_t)(NW / KSPLIT) * (KSPLIT - 1) * 64 * 16 * TN * 4;
@@ -1823,9 +1839,7 @@ hipError_t run_decode_lds(KParams kp, int parts, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  const hipError_t attr = allow_full_lds<&gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L>>();
   if (attr != hipSuccess) return attr;
   gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
   return hipGetLastError();
@@ -1921,8 +1935,7 @@ hipError_t run_decode2(KParams kp, hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode2_kernel<BN, KG, KPW, NW, L, kPow2>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+  const hipError_t attr = allow_full_lds<&gemm_decode2_kernel<BN, KG, KPW, NW, L, kPow2>>();
   if (attr != hipSuccess) return attr;
   gemm_decode2_kernel<BN, KG, KPW, NW, L, kPow2><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
   return hipGetLastError();
@@ -1941,13 +1954,11 @@ hipError_t run_decode3(KParams kp, hipStream_t s) {
   if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
   kp.nwg = (int)nwg;
   if (kp.pow2) {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode3_kernel<WM, WN, TN, S, L, true>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    const hipError_t attr = allow_full_lds<&gemm_decode3_kernel<WM, WN, TN, S, L, true>>();
     if (attr != hipSuccess) return attr;
     gemm_decode3_kernel<WM, WN, TN, S, L, true><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
   } else {
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_decode3_kernel<WM, WN, TN, S, L, false>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    const hipError_t attr = allow_full_lds<&gemm_decode3_kernel<WM, WN, TN, S, L, false>>();
     if (attr != hipSuccess) return attr;
     gemm_decode3_kernel<WM, WN, TN, S, L, false><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
   }
