@@ -70,7 +70,7 @@ def _L():
         lib.dgo_cast_per_block_pow2.argtypes = [P, I64, I64, P, P]
         lib.dgo_bf16_to_f32.argtypes = [P, I64, P]
         lib.dgo_gemm.argtypes = [P, P, P, P, I64, I64, I64, P]
-        lib.dgo_gemm_pairs.argtypes = [P, P, P, P, P, I64, I64, P, P, I64, P]
+        lib.dgo_gemm_pairs.argtypes = [P, P, P, P, P, I32, I64, I64, P, P, I64, P]
         lib.dgo_grouped_contiguous.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P]
         lib.dgo_grouped_masked.argtypes = [P, P, P, P, P, I32, I64, I64, I64, P]
         lib.dgo_block_sums.argtypes = [P, P, I64, I64, I64, P]
@@ -175,15 +175,21 @@ def gemm(a, sa, b, sb) -> np.ndarray:
 
 def gemm_pairs(a, sa, b, sb, rows, cols, group_of_row=None) -> np.ndarray:
     """R at selected (rows[i], cols[i]). a [Mrows,K]; b [G,N,K] or [N,K]; row m uses
-    group group_of_row[m] (default 0)."""
+    group group_of_row[m] (default 0); a row whose group is outside [0, G) gives NaN."""
     a = _c(a, np.uint8); b = _c(b, np.uint8)
     sa = _c(sa, np.float32); sb = _c(sb, np.float32)
     K = a.shape[-1]
     N = b.shape[-2]
+    G = b.shape[0] if b.ndim == 3 else 1
+    assert b.shape[-1] == K and sa.shape == (a.shape[0], K // QBLK)
+    assert sb.shape[-2:] == (N // QBLK, K // QBLK) and (sb.shape[0] if sb.ndim == 3 else 1) == G
     rows = _c(rows, np.int64); cols = _c(cols, np.int64)
+    assert rows.shape == cols.shape
+    assert rows.size == 0 or (rows.min() >= 0 and rows.max() < a.shape[0] and cols.min() >= 0 and cols.max() < N)
     gr = None if group_of_row is None else _c(group_of_row, np.int32)
+    assert gr is None or gr.shape == (a.shape[0],)
     out = np.empty(rows.shape, np.float64)
-    _L().dgo_gemm_pairs(_p(a), _p(sa), _p(b), _p(sb), _p(gr), N, K, _p(rows), _p(cols),
+    _L().dgo_gemm_pairs(_p(a), _p(sa), _p(b), _p(sb), _p(gr), G, N, K, _p(rows), _p(cols),
                         rows.size, _p(out))
     return out
 

@@ -269,16 +269,19 @@ void dgo_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* 
 }
 
 /* Selected output elements. Row m of `a` uses group g = group_of_row[m] (or 0 when the
- * pointer is NULL): b and sb are [G,N,K] and [G,N/128,K/128]. */
+ * pointer is NULL): b and sb are [G,N,K] and [G,N/128,K/128]. A row whose group lies
+ * outside [0, G) (a padding row, -1) gets NaN, as in dgo_grouped_contiguous. */
 void dgo_gemm_pairs(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
-                    const int32_t* group_of_row, int64_t N, int64_t K, const int64_t* rows,
-                    const int64_t* cols, int64_t count, double* out) {
+                    const int32_t* group_of_row, int32_t G, int64_t N, int64_t K,
+                    const int64_t* rows, const int64_t* cols, int64_t count, double* out) {
   int64_t bstride = N * K, sbstride = (N / QBLK) * (K / QBLK);
 #pragma omp parallel for schedule(dynamic, 64)
   for (int64_t i = 0; i < count; ++i) {
     int64_t m = rows[i];
     int64_t g = group_of_row ? group_of_row[m] : 0;
-    out[i] = gemm_element(a, sa, b + g * bstride, sb + g * sbstride, m, cols[i], K);
+    out[i] = (g < 0 || g >= G)
+                 ? NAN
+                 : gemm_element(a, sa, b + g * bstride, sb + g * sbstride, m, cols[i], K);
   }
 }
 

@@ -340,6 +340,61 @@ def test_gemm_pairs_equal_full_gemm():
     assert np.array_equal(oracle.gemm_pairs(qa, sa, qb, sb, rows, cols), R[rows, cols])
 
 
+def _wrong_expert_stride(qb, sb):
+    """The expert weights as a kernel with a halved expert stride would read them: expert g's
+    slab starting g*N*K/2 bytes (and g*(N/128)*(K/128)/2 scales) into the stacked tensors."""
+    G, N, K = qb.shape
+    fb, fs = qb.reshape(-1), sb.reshape(-1)
+    nb, ns = N * K, sb.shape[1] * sb.shape[2]
+    bad_b = np.stack([fb[g * nb // 2: g * nb // 2 + nb].reshape(N, K) for g in range(G)])
+    bad_s = np.stack([fs[g * ns // 2: g * ns // 2 + ns].reshape(sb.shape[1:]) for g in range(G)])
+    return bad_b, bad_s
+
+
+def test_gemm_pairs_grouped_equals_grouped_oracles():
+    # the sampled form used by the full-size grouped parity checks, pinned against the
+    # contiguous and masked oracles (themselves pinned to the dense one per expert below)
+    G, N, K = 4, 256, 384
+    a, b, mi = synth.contiguous_inputs(G, 300, N, K, seed=33)
+    qa, sa = oracle.cast_per_token(a)
+    qb, sb = oracle.cast_per_block(b.reshape(G * N, K))
+    qb, sb = qb.reshape(G, N, K), sb.reshape(G, N // 128, K // 128)
+    Rc = oracle.grouped_contiguous(qa, sa, qb, sb, mi)
+    r = synth.rng(33, 7)
+    rows, cols = r.integers(0, mi.size, 3000), r.integers(0, N, 3000)
+    got = oracle.gemm_pairs(qa, sa, qb, sb, rows, cols, group_of_row=mi)
+    pad = mi[rows] < 0
+    assert pad.any() and (~pad).any()
+    assert np.isnan(got[pad]).all()  # padding rows (-1): NaN, never a read before b
+    assert np.array_equal(got[~pad], Rc[rows[~pad], cols[~pad]])
+    # planted mistakes: a halved expert stride, and the expert of every row taken as 0
+    bad_b, bad_s = _wrong_expert_stride(qb, sb)
+    wrong = oracle.gemm_pairs(qa, sa, bad_b, bad_s, rows[~pad], cols[~pad], group_of_row=mi)
+    assert not oracle.compare(wrong, Rc[rows[~pad], cols[~pad]])["ok"]
+    zero = oracle.gemm_pairs(qa, sa, qb, sb, rows[~pad], cols[~pad], group_of_row=np.zeros_like(mi))
+    assert not oracle.compare(zero, Rc[rows[~pad], cols[~pad]])["ok"]
+    # out-of-range groups give NaN as well
+    assert np.isnan(oracle.gemm_pairs(qa, sa, qb, sb, rows[:4], cols[:4],
+                                      group_of_row=np.full_like(mi, G))).all()
+
+    # masked layout: rows of [G*M_max, K] with group r // M_max
+    M_max = 96
+    am, bm, mm = synth.masked_inputs(G, M_max, N, K, seed=34)
+    qam, sam = oracle.cast_per_token(am.reshape(G * M_max, K))
+    qbm, sbm = oracle.cast_per_block(bm.reshape(G * N, K))
+    qbm, sbm = qbm.reshape(G, N, K), sbm.reshape(G, N // 128, K // 128)
+    full = np.full(G, M_max, np.int32)
+    Rm = oracle.grouped_masked(qam.reshape(G, M_max, K), sam.reshape(G, M_max, K // 128), qbm, sbm, full)
+    Rm = Rm.reshape(G * M_max, N)
+    group = (np.arange(G * M_max) // M_max).astype(np.int32)
+    rows, cols = r.integers(0, G * M_max, 2000), r.integers(0, N, 2000)
+    got = oracle.gemm_pairs(qam, sam, qbm, sbm, rows, cols, group_of_row=group)
+    assert np.array_equal(got, Rm[rows, cols])
+    bad_b, bad_s = _wrong_expert_stride(qbm, sbm)
+    wrong = oracle.gemm_pairs(qam, sam, bad_b, bad_s, rows, cols, group_of_row=group)
+    assert not oracle.compare(wrong, Rm[rows, cols])["ok"]
+
+
 # ---------------------------------------------------------------------------------
 # grouped layouts
 # ---------------------------------------------------------------------------------
