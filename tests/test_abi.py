@@ -37,6 +37,20 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_library_exports_only_the_c_abi(L):
+    # the dynamic symbol table holds exactly the dg_* functions the header declares: no C++
+    # internals or compiler-generated symbols another loaded library could bind to
+    import shutil
+    import subprocess
+    import moe_grouped_gemm_e4m3_amd as m
+    nm = shutil.which("nm") or shutil.which("llvm-nm")
+    if nm is None:
+        pytest.skip("no nm on PATH")
+    out = subprocess.run([nm, "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert exported == _declared_functions()
+
+
 def test_status_strings(L):
     for code, name in [(0, b"DG_OK"), (1, b"DG_ERR_INVALID_ARGUMENT"), (2, b"DG_ERR_UNSUPPORTED_SHAPE"),
                        (3, b"DG_ERR_MISALIGNED"), (4, b"DG_ERR_UNSUPPORTED_DEVICE"), (5, b"DG_ERR_LAUNCH")]:
