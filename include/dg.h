@@ -24,9 +24,15 @@
  *     and 16-byte aligned. The library never allocates, frees or keeps a pointer.
  *   - Activation scales (sfa) are stored K-block-major: [K/128][M], i.e. for each
  *     128-wide K block the scales of all M rows are contiguous (with a leading [G] for
- *     the masked layout). The pages leave the layout open; this one lets a GEMM tile
- *     fetch the scales of its rows for one K block as one contiguous run. Weight scales
- *     (sfb) are [N/128][K/128].
+ *     the masked layout). This is NOT the row-major [M][K/128] layout a reader might
+ *     assume: both have M*K/128 elements, so a caller that passes row-major scales gets
+ *     wrong results with no error (the library cannot tell them apart). The pages leave
+ *     the layout open. K-block-major lets a GEMM tile fetch the scales of its rows for one
+ *     K block as one contiguous run of cache lines; stored row-major, the 32 scales one
+ *     wave needs per K block lay in 32 different lines, which cost about a third of the
+ *     prefill kernel's load time. The per-token cast writes this layout directly (its G
+ *     argument gives the masked layout's [G][K/128][M_max]). Weight scales (sfb) are
+ *     [N/128][K/128].
  *   - FP8 tensors are raw OCP E4M3FN bytes (uint8_t); bf16 tensors are raw uint16_t bits.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls only
  *     enqueue work on it and return without synchronising; inputs must stay alive
