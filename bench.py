@@ -1,23 +1,26 @@
 """Benchmark of the FP8 block-scaled GEMM path on one MI355X.
 
-Default workload: dense decode, M = 64 tokens, two DeepSeek-V3-shaped layers
-(N=7168, K=2048) and (N=24576, K=1536). One step = the per-token FP8 cast of each
-layer's fp32 activations followed by its block-scaled FP8 GEMM (bf16 out), for both layers.
-Inputs are resident in HBM before timing starts. Each step uses one of R copies of the
-weights (R * |weights| >= 512 MiB) so the 256 MiB Infinity Cache cannot serve them.
+Default workload ("decode", dense + grouped at decode): two dense DeepSeek-V3-shaped layers
+at M = 64 tokens, (N=7168, K=2048) and (N=24576, K=1536), and the two MoE expert layers in
+the masked layout one GPU holds at decode (G=32 experts, 256-row buffers, valid rows
+~U{0..256}), (N=4096, K=7168) and (N=7168, K=2048). One step = for each layer, the per-token
+FP8 cast of its fp32 activations followed by its block-scaled FP8 GEMM (bf16 out).
+Inputs are resident in HBM before timing starts. Every layer cycles through R_l copies of
+its weights (R_l * |weights_l| >= 512 MiB) so the 256 MiB Infinity Cache cannot serve them.
 
 Steps are captured in HIP graphs (one graph per weight copy, launched on torch's stream)
 and replayed, so the measurement is GPU time rather than Python launch overhead.
 
 Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included).
-`roofline` is for the kernel that takes the most time in the step; its average duration
-comes from HIP events around graphs of back-to-back launches of that kernel alone, on the
-stream it runs on. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
+`roofline` is for the kernel that takes the most time in the step; its duration comes from
+HIP events, on the stream it runs on, around replays of a graph of back-to-back launches of
+that kernel alone (one per weight copy): at least 100 launches and 10 replays per kernel,
+and the median over the replays. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
 of the same workload. `traffic` (HBM bytes per launch) is read from profiles/traffic.json
 when that file was produced from the current kernel source.
 
-Other workloads (--workload prefill|contiguous|masked|ffn_contiguous|ffn_masked|ffn_masked_decode|tiny)
-print the same line shape.
+Other workloads (--workload decode_dense|skinny128|skinny256|prefill|contiguous|masked|
+ffn_contiguous|ffn_masked|ffn_masked_decode|tiny) print the same line shape.
 --ue8m0 runs the same steps with power-of-two (UE8M0) scales: the _ue8m0 casts and GEMMs.
 """
 from __future__ import annotations
@@ -40,8 +43,19 @@ RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
 
 # (kind, shape) per layer of each workload
 WORKLOADS = {
-    "decode": {"desc": "dense decode M=64: (N=7168,K=2048) + (N=24576,K=1536)",
-               "layers": [("dense", dict(M=64, N=7168, K=2048)), ("dense", dict(M=64, N=24576, K=1536))]},
+    # the metric's configuration: dense decode at M=64 and the MoE masked (decode) layout
+    "decode": {"desc": "dense M=64: (N=7168,K=2048) + (N=24576,K=1536); MoE masked G=32, M_max=256, "
+                       "valid ~U{0..256}: (N=4096,K=7168) + (N=7168,K=2048)",
+               "layers": [("dense", dict(M=64, N=7168, K=2048)), ("dense", dict(M=64, N=24576, K=1536)),
+                          ("masked", dict(G=32, M_max=256, N=4096, K=7168)),
+                          ("masked", dict(G=32, M_max=256, N=7168, K=2048))]},
+    "decode_dense": {"desc": "dense decode M=64: (N=7168,K=2048) + (N=24576,K=1536)",
+                     "layers": [("dense", dict(M=64, N=7168, K=2048)), ("dense", dict(M=64, N=24576, K=1536))]},
+    # skinny M between decode and prefill, on the decode layers' shapes
+    "skinny128": {"desc": "dense M=128: (N=7168,K=2048) + (N=24576,K=1536)",
+                  "layers": [("dense", dict(M=128, N=7168, K=2048)), ("dense", dict(M=128, N=24576, K=1536))]},
+    "skinny256": {"desc": "dense M=256: (N=7168,K=2048) + (N=24576,K=1536)",
+                  "layers": [("dense", dict(M=256, N=7168, K=2048)), ("dense", dict(M=256, N=24576, K=1536))]},
     "prefill": {"desc": "dense prefill M=4096 with 1% x50 outliers: (N=7168,K=18432) + (N=36864,K=7168)",
                 "layers": [("dense", dict(M=4096, N=7168, K=18432, outliers=True)),
                            ("dense", dict(M=4096, N=36864, K=7168, outliers=True))]},
@@ -330,8 +344,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ue8m0", action="store_true", help="power-of-two (UE8M0) scales")
-    ap.add_argument("--kernel-reps", type=int, default=0,
-                    help="launches per kernel in the per-kernel timing (default: steps)")
+    ap.add_argument("--kernel-reps", type=int, default=100,
+                    help="launches per kernel in the per-kernel timing (at least 100)")
     ap.add_argument("--cache-bytes", type=float, default=512 * 2 ** 20,
                     help="minimum bytes of distinct weight copies cycled through")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -351,11 +365,13 @@ def main():
     torch.cuda.set_device(0)
 
     wl = WORKLOADS[args.workload]
-    # weight copies so each step streams its weights from HBM, not the 256 MiB cache
-    wbytes = sum(weight_elems(kind, s) for kind, s in wl["layers"])
-    copies = int(min(64, max(1, math.ceil(args.cache_bytes / wbytes))))
-    layers = [build_layer(dg, torch, kind, s, args.seed + i, copies, args.ue8m0)
+    # weight copies per layer, so that every launch streams its weights from HBM, not from the
+    # 256 MiB cache, in the step and in the per-kernel timing alike
+    layer_copies = [int(min(64, max(1, math.ceil(args.cache_bytes / weight_elems(kind, s)))))
+                    for kind, s in wl["layers"]]
+    layers = [build_layer(dg, torch, kind, s, args.seed + i, layer_copies[i], args.ue8m0)
               for i, (kind, s) in enumerate(wl["layers"])]
+    copies = max(layer_copies)  # one step graph per index; layer l uses copy index % R_l
     torch.cuda.synchronize()
 
     if args.copy_calibration:
@@ -379,8 +395,9 @@ def main():
 
     warm_clocks(torch, step_graphs, 0.5)
 
-    # per-kernel timing: graphs of back-to-back launches of one kernel, same weight copies
-    reps = args.kernel_reps or args.steps
+    # per-kernel timing: graphs of back-to-back launches of one kernel over the layer's
+    # weight copies, replayed until at least `reps` launches and 10 replays
+    reps = max(100, args.kernel_reps)
     kernels = []
     step_flops = 0.0
     for L in layers:
@@ -427,17 +444,19 @@ def main():
             timed.append(("gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
                                                                    *L["ws"][c % len(L["ws"])][:2], L["d"]),
                           layer_work(kind, s_, L["valid"], L["active"]), True))
+        lc = len(L["ws"])
         for lab, fn, (f, b), in_step in timed:
-            gr = capture(torch, lambda fn=fn: [fn(c) for c in range(copies)])
-            n = max(1, reps // copies)
+            gr = capture(torch, lambda fn=fn, lc=lc: [fn(c) for c in range(lc)])
+            n = max(10, math.ceil(reps / lc))
             time_graphs(torch, [gr], 2)
-            ms = time_graphs(torch, [gr], n)
-            avg_us = ms / (n * copies) * 1e3
+            per = sorted(time_graphs(torch, [gr], 1) / lc * 1e3 for _ in range(n))
+            avg_us = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
             bound = "hbm" if (f == 0.0 or f / b < RIDGE) else "mfma"
             layer = kind if ffn else "%s N=%d K=%d" % (kind, s_["N"], K)
             kernels.append({"kernel": lab, "layer": layer, "avg_us": avg_us,
                             "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
-                            "bound": bound, "flops": f, "bytes": b, "launches": n * copies, "in_step": in_step})
+                            "bound": bound, "flops": f, "bytes": b, "launches": n * lc, "replays": n,
+                            "mean_us": sum(per) / len(per), "in_step": in_step})
             del gr
     dom = max((k for k in kernels if k["in_step"]), key=lambda k: k["avg_us"])
 
@@ -457,7 +476,7 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-        "config": {"workload": wl["desc"], "weight_copies": copies,
+        "config": {"workload": wl["desc"], "weight_copies": layer_copies,
                    "scales": "UE8M0 (powers of two)" if args.ue8m0 else "fp32 (amax / 448)",
                    "step": ("per-token FP8 cast of fp32 activations + expert FFN: gate/up GEMM with fused "
                             "SwiGLU and FP8 re-cast, then the down GEMM (bf16 out); replayed from HIP graphs"

@@ -236,6 +236,19 @@ dg_status_t dg_moe_ffn_fp8(int32_t layout, int32_t scale_fmt, const uint8_t* x, 
                            const int32_t* meta, uint8_t* hq, float* sfh, uint16_t* y, int32_t G, int64_t M,
                            int64_t H, int64_t I, int64_t expected_m, void* stream);
 
+/*
+ * Plain fp32 -> e4m3 conversion with gfx950's hardware instruction, the conversion the fused
+ * SwiGLU epilogue of dg_gemm_fp8_swiglu applies to h / s (its quotients never exceed
+ * 448.0001). OCP E4M3FN codes (DeepSeek-V3 repo review, "Risks" item 6: bound 448), round to
+ * nearest even, sign of zero kept. It exists so that this conversion can be checked against
+ * the per-token cast's rule on every input of interest.
+ *   x [n] fp32 (device), q [n] e4m3 bytes (device, output); n % 4 == 0.
+ * Precondition: |x| <= 464 and finite. Within it the result equals the saturating encoder of
+ * dg_cast_fp8_per_token (values in (448, 464] round to 448); beyond it the hardware does not
+ * saturate and the codes are unspecified (never a fault).
+ */
+dg_status_t dg_convert_fp8_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status_t status);
 

@@ -15,6 +15,7 @@ Entry points (same names as the C ABI, without the dg_ prefix):
   cast_fp8_per_token(x)                      -> (q [M,K] uint8, sf [K/128,M] fp32)
                                                 (x [G,M,K] -> q [G,M,K], sf [G,K/128,M])
   cast_fp8_per_block(w)                      -> (q [N,K] uint8, sf [N/128,K/128] fp32)
+  convert_fp8_e4m3(x)                        -> q uint8: the hardware conversion of the SwiGLU epilogue
   gemm_fp8_nt(a, sfa, b, sfb)                -> d [M,N] bf16
   grouped_gemm_contiguous(a, sfa, b, sfb, m_indices)      -> d [M_total,N] bf16
   grouped_gemm_masked(a, sfa, b, sfb, masked_m, expected_m) -> d [G,M_max,N] bf16
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_swiglu.argtypes = [I32, I32, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_moe_ffn_fp8.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_gemm_fp8_scheduled.restype = ctypes.c_int
+        L.dg_convert_fp8_e4m3.argtypes = [P, I64, P, P]
+        L.dg_convert_fp8_e4m3.restype = ctypes.c_int
         L.dg_status_string.argtypes = [ctypes.c_int]
         L.dg_status_string.restype = ctypes.c_char_p
         L.dg_last_error_message.argtypes = []
@@ -141,6 +144,18 @@ def cast_fp8_per_block(w: torch.Tensor, q: torch.Tensor | None = None, sf: torch
     fn = lib().dg_cast_fp8_per_block_ue8m0 if ue8m0 else lib().dg_cast_fp8_per_block
     _check(fn(_ptr(w), dt, rows, K, _ptr(q), _ptr(sf), _stream(w.device)))
     return q, sf
+
+
+def convert_fp8_e4m3(x: torch.Tensor, q: torch.Tensor | None = None) -> torch.Tensor:
+    """x fp32 (any shape, numel % 4 == 0, |x| <= 464) -> e4m3 codes (uint8, same shape) from
+    the hardware conversion the fused SwiGLU epilogue uses."""
+    _need(x, torch.float32, "x")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    _need(q, torch.uint8, "q")
+    if q.numel() != x.numel():
+        raise ValueError("q must have x's size")
+    _check(lib().dg_convert_fp8_e4m3(_ptr(x), x.numel(), _ptr(q), _stream(x.device)))
+    return q
 
 
 # ---- GEMMs ---------------------------------------------------------------------------

@@ -267,6 +267,18 @@ dg_status_t dg_moe_ffn_fp8(int32_t layout, int32_t scale_fmt, const uint8_t* x, 
                   L == dg::Layout::Dense ? 1 : G, M, H, I, expected_m, stream, name);
 }
 
+dg_status_t dg_convert_fp8_e4m3(const float* x, int64_t n, uint8_t* q, void* stream) {
+  const char* name = "dg_convert_fp8_e4m3";
+  if (n < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
+  if (n % 4 != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: n=%lld is not a multiple of 4", name, (long long)n);
+  if (n == 0) return ok();
+  if (!x || !q) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(x) || !aligned16(q)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  const dg_status_t st = check_device();
+  if (st != DG_OK) return st;
+  return launched(dg::launch_convert_e4m3(x, q, n, static_cast<hipStream_t>(stream)), name);
+}
+
 const char* dg_status_string(dg_status_t status) {
   switch (status) {
     case DG_OK: return "DG_OK";

@@ -100,6 +100,16 @@ __global__ __launch_bounds__(256) void cast_per_block_kernel(const void* __restr
   if (t == 0) sf[bn * kblocks + bk] = s;
 }
 
+// Plain conversion of fp32 values (already divided by their scale) with the hardware
+// conversion of the fused SwiGLU epilogue: 4 values per thread, grid-stride.
+__global__ __launch_bounds__(256) void convert_e4m3_kernel(const float4* __restrict__ x, uint32_t* __restrict__ q,
+                                                           int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    const float4 v = x[i];
+    q[i] = e4m3_hw_pack4(v.x, v.y, v.z, v.w);
+  }
+}
+
 template <bool kPow2>
 hipError_t cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q, float* sf,
                           hipStream_t stream) {
@@ -135,6 +145,15 @@ hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, i
                                  float* sf, hipStream_t stream) {
   return pow2 ? cast_per_token<true>(x, bf16, G, M, K, q, sf, stream)
               : cast_per_token<false>(x, bf16, G, M, K, q, sf, stream);
+}
+
+hipError_t launch_convert_e4m3(const float* x, uint8_t* q, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  int64_t blocks = (n4 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  convert_e4m3_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(reinterpret_cast<const float4*>(x),
+                                                                         reinterpret_cast<uint32_t*>(q), n4);
+  return hipGetLastError();
 }
 
 hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q,

@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
   return sign | code;
 }
 
+// Four fp32 values -> four e4m3 codes (byte i = code of value i) with gfx950's conversion
+// instruction (v_cvt_pk_fp8_f32: OCP E4M3FN, round to nearest even). It does not saturate:
+// it agrees with e4m3_encode for |y| <= 464 (below the midpoint between 448 and 480 every
+// value rounds to at most 448), which callers must guarantee.
+__device__ __forceinline__ uint32_t e4m3_hw_pack4(float y0, float y1, float y2, float y3) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, (int)lo, true);
+}
+
 // The smallest power of two >= v (v >= 0), and >= 2^-126, from the fp32 bits: a normal v
 // with a zero mantissa is a power of two already; otherwise the exponent goes up by one.
 // This is the UE8M0 (power-of-two) scale of the casts.

@@ -1296,8 +1296,7 @@ __device__ __forceinline__ void swg_quant(const v4f (&hv)[TH][TN], const float* 
           x[r] = sv[r] == 0.0f ? h * 0.0f : (sv[r] >= kTiny ? fmaf(fmaf(-q0, sv[r], h), rv[r], q0) : h / sv[r]);
         }
       }
-      uint32_t P = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-      P = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], (int)P, true);
+      uint32_t P = e4m3_hw_pack4(x[0], x[1], x[2], x[3]);  // |x| <= 448.0001 here
       uint32_t Q = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0x4E, 0xF, 0xF, true);  // lane ^ 2
       P = __builtin_amdgcn_perm(Q, P, selA);
       Q = (uint32_t)__builtin_amdgcn_mov_dpp((int)P, 0xB1, 0xF, 0xF, true);           // lane ^ 1

@@ -51,6 +51,14 @@ def test_library_exports_only_the_c_abi(L):
     assert exported == _declared_functions()
 
 
+def test_convert_argument_errors(L):
+    assert L.dg_convert_fp8_e4m3(P, 6, P, None) == 2   # not a multiple of 4
+    assert L.dg_convert_fp8_e4m3(P, -4, P, None) == 1
+    assert L.dg_convert_fp8_e4m3(None, 8, P, None) == 1
+    assert L.dg_convert_fp8_e4m3(Q, 8, P, None) == 3
+    assert L.dg_convert_fp8_e4m3(None, 0, None, None) == 0  # empty: nothing enqueued
+
+
 def test_status_strings(L):
     for code, name in [(0, b"DG_OK"), (1, b"DG_ERR_INVALID_ARGUMENT"), (2, b"DG_ERR_UNSUPPORTED_SHAPE"),
                        (3, b"DG_ERR_MISALIGNED"), (4, b"DG_ERR_UNSUPPORTED_DEVICE"), (5, b"DG_ERR_LAUNCH")]:

@@ -98,6 +98,85 @@ def test_cast_conversion_sweep(dg):
     assert_same_bytes(q, qo, "sweep q")
 
 
+FP32_448 = 0x43E00000  # bit pattern of 448.0
+FP32_464 = 0x43E80000  # bit pattern of 464.0
+
+
+def _exhaustive_batches(hi_bits: int, per: int, batch: int):
+    """[start, end) ranges of fp32 bit patterns covering 0 .. hi_bits inclusive."""
+    start = 0
+    while start <= hi_bits:
+        end = min(hi_bits + 1, start + per * batch)
+        yield start, end
+        start = end
+
+
+def _values(start: int, end: int, n_pad: int, negative: bool, device=None):
+    """fp32 values with bit patterns start..end-1, then n_pad zeros; negated for the other sign
+    (negation flips the sign bit exactly, +0 included)."""
+    if device is None:
+        bits = np.arange(start, end + n_pad, dtype=np.uint32)
+        bits[end - start:] = 0
+        v = bits.view(np.float32)
+        return -v if negative else v
+    bits = torch.arange(start, end + n_pad, dtype=torch.int64, device=device)
+    bits[end - start:] = 0
+    v = bits.to(torch.int32).view(torch.float32)
+    return -v if negative else v
+
+
+@pytest.mark.slow
+def test_cast_conversion_exhaustive(dg):
+    # every fp32 value with |x| <= 448, both signs, through the per-token cast: 127 values per
+    # 128-element chunk whose first element is 448, so that amax = 448, s = 1 exactly and every
+    # value is encoded as itself; compared byte for byte with the oracle's encoder
+    per, batch = 127, 1 << 20
+    total = 0
+    for negative in (False, True):
+        for start, end in _exhaustive_batches(FP32_448, per, batch):
+            n = end - start
+            nch = (n + per - 1) // per
+            pad = nch * per - n
+            say("cast exhaustive sweep sign=%s bits [%#x, %#x)" % ("-" if negative else "+", start, end))
+            x = torch.empty((nch, 128), dtype=torch.float32, device="cuda:0")
+            x[:, 0] = 448.0
+            x[:, 1:] = _values(start, end, pad, negative, "cuda:0").view(nch, per)
+            q, s = dg.cast_fp8_per_token(x)
+            qh = q.cpu().numpy()
+            assert (s.cpu().numpy() == 1.0).all()
+            assert (qh[:, 0] == 0x7E).all()
+            expect = oracle.encode(_values(start, end, pad, negative))
+            got = qh[:, 1:].reshape(-1)
+            bad = np.nonzero(got != expect)[0]
+            assert bad.size == 0, "%d mismatches, first at bits %#x: gpu %#x oracle %#x" % (
+                bad.size, start + bad[0], got[bad[0]], expect[bad[0]])
+            total += n
+            del x, q, s
+    assert total == 2 * (FP32_448 + 1)
+
+
+@pytest.mark.slow
+def test_hw_conversion_exhaustive(dg):
+    # every fp32 value with |x| <= 464, both signs, through the hardware conversion that the
+    # fused SwiGLU epilogue uses (dg_convert_fp8_e4m3), against the oracle's saturating encoder
+    batch = 1 << 27
+    total = 0
+    for negative in (False, True):
+        for start, end in _exhaustive_batches(FP32_464, 1, batch):
+            n = end - start
+            pad = (-n) % 4
+            say("hardware conversion exhaustive sign=%s bits [%#x, %#x)" % ("-" if negative else "+", start, end))
+            x = _values(start, end, pad, negative, "cuda:0")
+            got = dg.convert_fp8_e4m3(x).cpu().numpy()[:n]
+            expect = oracle.encode(_values(start, end, 0, negative))
+            bad = np.nonzero(got != expect)[0]
+            assert bad.size == 0, "%d mismatches, first at bits %#x: gpu %#x oracle %#x" % (
+                bad.size, start + bad[0], got[bad[0]], expect[bad[0]])
+            total += n
+            del x
+    assert total == 2 * (FP32_464 + 1)
+
+
 def test_cast_bf16_input(dg):
     x = synth.with_outliers(synth.normal((40, 768), 8, synth.TID_A), 8)
     xb = torch.from_numpy(x).to(torch.bfloat16)
