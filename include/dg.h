@@ -237,6 +237,27 @@ dg_status_t dg_moe_ffn_fp8(int32_t layout, int32_t scale_fmt, const uint8_t* x, 
                            int64_t H, int64_t I, int64_t expected_m, void* stream);
 
 /*
+ * dg_moe_ffn_fp8 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same two launches,
+ * the same arguments minus hq and sfh, and the same results. The FP8 activation between the
+ * GEMMs lives in a static device array of the library instead of a caller workspace.
+ *   - The array holds 32 MiB (33554432 bytes) on every GPU the library runs on, from the
+ *     first call on that GPU until the process ends. A call needs rows*I bytes (rounded up to
+ *     256) plus 4*rows*I/128 bytes of scales, rows = M (masked: G*M_max); larger calls return
+ *     DG_ERR_UNSUPPORTED_SHAPE before anything is enqueued (e.g. I = 2048 allows 15887 rows).
+ *   - No memory is allocated or freed, by the library or any routine it calls. The first call
+ *     on a GPU looks up the array's device address (hipGetSymbolAddress) and keeps it.
+ *   - Every call on one GPU uses the same array and leaves its contents there. Nothing in it
+ *     needs to start at zero (each call writes every value its down GEMM's stored results
+ *     read). Calls that overlap on one GPU (several streams, or host threads) race on it:
+ *     order them, e.g. on one stream.
+ */
+dg_status_t dg_moe_ffn_fp8_noalloc(int32_t layout, int32_t scale_fmt, const uint8_t* x, const float* sfx,
+                                   const uint8_t* w1, const float* sfw1, const uint8_t* w2, const float* sfw2,
+                                   const int32_t* meta, uint16_t* y, int32_t G, int64_t M, int64_t H, int64_t I,
+                                   int64_t expected_m, void* stream);
+
+/*
  * Plain fp32 -> e4m3 conversion with gfx950's hardware instruction, the conversion the fused
  * SwiGLU epilogue of dg_gemm_fp8_swiglu applies to h / s (its quotients never exceed
  * 448.0001). OCP E4M3FN codes (DeepSeek-V3 repo review, "Risks" item 6: bound 448), round to

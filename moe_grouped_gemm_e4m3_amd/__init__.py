@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.dg_gemm_fp8_swiglu.argtypes = [I32, I32, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_moe_ffn_fp8.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_gemm_fp8_scheduled.restype = ctypes.c_int
+        L.dg_moe_ffn_fp8_noalloc.argtypes = [I32, I32, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
+        L.dg_moe_ffn_fp8_noalloc.restype = ctypes.c_int
         L.dg_convert_fp8_e4m3.argtypes = [P, I64, P, P]
         L.dg_convert_fp8_e4m3.restype = ctypes.c_int
         L.dg_status_string.argtypes = [ctypes.c_int]
@@ -311,3 +313,28 @@ def moe_ffn_fp8(layout, x, sfx, w1, sfw1, w2, sfw2, meta=None, expected_m: int =
                               _ptr(y), G, M, H, I, expected_m, _stream(x.device))
     _check(st)
     return y, hq, sfh
+
+
+def moe_ffn_fp8_noalloc(layout, x, sfx, w1, sfw1, w2, sfw2, meta=None, expected_m: int = 0, y=None,
+                        ue8m0: bool = False):
+    """moe_ffn_fp8 with the FP8 activation between the GEMMs held in the library's static
+    device scratch (dg_moe_ffn_fp8_noalloc): no workspace argument. Returns y."""
+    _operands(x, sfx, w1, sfw1)
+    _need(w2, torch.uint8, "w2")
+    _need(sfw2, torch.float32, "sfw2")
+    G, M, H, I, _, _ = _ffn_shapes(layout, x, sfx, w1, sfw1, meta)
+    want_w2 = (G, H, I) if (layout != LAYOUT_DENSE or w2.dim() == 3) else (H, I)
+    if tuple(w2.shape) != want_w2 or tuple(sfw2.shape) != want_w2[:-2] + (H // 128, I // 128):
+        raise ValueError("shape mismatch: w2 %s sfw2 %s" % (tuple(w2.shape), tuple(sfw2.shape)))
+    if meta is not None:
+        _need(meta, torch.int32, "meta")
+    y_shape = (G, M, H) if layout == LAYOUT_MASKED else (M, H)
+    y = torch.empty(y_shape, dtype=torch.bfloat16, device=x.device) if y is None else y
+    _need(y, torch.bfloat16, "y")
+    if tuple(y.shape) != y_shape:
+        raise ValueError("y shape mismatch")
+    st = lib().dg_moe_ffn_fp8_noalloc(layout, SCALE_UE8M0 if ue8m0 else SCALE_F32, _ptr(x), _ptr(sfx), _ptr(w1),
+                                      _ptr(sfw1), _ptr(w2), _ptr(sfw2), None if meta is None else _ptr(meta),
+                                      _ptr(y), G, M, H, I, expected_m, _stream(x.device))
+    _check(st)
+    return y

@@ -165,6 +165,42 @@ dg_status_t run_swiglu(int32_t layout, int32_t scale_fmt, const uint8_t* a, cons
   return launched(e, name);
 }
 
+// ---- static scratch for the entry point that allocates nothing ------------------------
+// The FP8 activation between the FFN's two GEMMs (hq, then its scales sfh) lives in this
+// file-scope device array for callers that cannot allocate. Each GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` only names the array: its
+// device address on the current GPU comes from hipGetSymbolAddress, once per device, and only
+// that address is ever handed to a kernel.
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of the current device's copy of `scratch` (looked up on the first call on
+// that device, under a mutex, and kept); nullptr with the error in *err on failure.
+uint8_t* scratch_address(hipError_t* err) {
+  static std::mutex mu;
+  static uint8_t* addr[64];
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    addr[dev] = static_cast<uint8_t*>(p);
+  }
+  *err = hipSuccess;
+  return addr[dev];
+}
+
+// Bytes of hq (rounded up to 256) and of sfh for an FFN call of `rows` rows.
+int64_t ffn_hq_bytes(int64_t rows, int64_t I) { return (rows * I + 255) / 256 * 256; }
+int64_t ffn_sfh_bytes(int64_t rows, int64_t I) { return 4 * rows * (I / kQ); }
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +313,41 @@ dg_status_t dg_convert_fp8_e4m3(const float* x, int64_t n, uint8_t* q, void* str
   const dg_status_t st = check_device();
   if (st != DG_OK) return st;
   return launched(dg::launch_convert_e4m3(x, q, n, static_cast<hipStream_t>(stream)), name);
+}
+
+dg_status_t dg_moe_ffn_fp8_noalloc(int32_t layout, int32_t scale_fmt, const uint8_t* x, const float* sfx,
+                                   const uint8_t* w1, const float* sfw1, const uint8_t* w2, const float* sfw2,
+                                   const int32_t* meta, uint16_t* y, int32_t G, int64_t M, int64_t H, int64_t I,
+                                   int64_t expected_m, void* stream) {
+  const char* name = "dg_moe_ffn_fp8_noalloc";
+  // every host-side check of dg_moe_ffn_fp8 first, with stand-in (aligned, never used)
+  // workspace pointers: the scratch size check and all argument errors need no device
+  uint8_t* const hq_stub = reinterpret_cast<uint8_t*>(256);
+  float* const sfh_stub = reinterpret_cast<float*>(512);
+  dg_status_t st = run_swiglu(layout, scale_fmt, x, sfx, w1, sfw1, meta, hq_stub, sfh_stub, G, M, I, H, expected_m,
+                              stream, name, true);
+  if (st != DG_OK) return st;
+  if (M == 0 || I == 0 || (layout != 0 && G == 0)) return ok();
+  if (!w2 || !sfw2 || !y) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  if (!aligned16(w2) || !aligned16(sfw2) || !aligned16(y))
+    return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  const int64_t rows = layout == 2 ? (int64_t)G * M : M;
+  const int64_t need = ffn_hq_bytes(rows, I) + ffn_sfh_bytes(rows, I);
+  if (need > kScratchBytes)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: the FP8 activation needs %lld bytes, above the %lld-byte static scratch",
+                name, (long long)need, (long long)kScratchBytes);
+  st = check_device();
+  if (st != DG_OK) return st;
+  hipError_t e = hipSuccess;
+  uint8_t* base = scratch_address(&e);
+  if (base == nullptr) return fail(DG_ERR_LAUNCH, "%s: scratch address: %s", name, hipGetErrorString(e));
+  uint8_t* hq = base;
+  float* sfh = reinterpret_cast<float*>(base + ffn_hq_bytes(rows, I));
+  st = run_swiglu(layout, scale_fmt, x, sfx, w1, sfw1, meta, hq, sfh, G, M, I, H, expected_m, stream, name, false);
+  if (st != DG_OK) return st;
+  const dg::Layout L = static_cast<dg::Layout>(layout);
+  return run_gemm(L, 0, scale_fmt == DG_SCALE_UE8M0, hq, sfh, w2, sfw2, L == dg::Layout::Dense ? nullptr : meta, y,
+                  L == dg::Layout::Dense ? 1 : G, M, H, I, expected_m, stream, name);
 }
 
 const char* dg_status_string(dg_status_t status) {

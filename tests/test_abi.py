@@ -51,6 +51,18 @@ def test_library_exports_only_the_c_abi(L):
     assert exported == _declared_functions()
 
 
+def test_ffn_noalloc_argument_errors(L):
+    f = L.dg_moe_ffn_fp8_noalloc
+    # masked G=1, M_max=15888, H=128, I=2048: 2112 bytes per row exceed the 32 MiB scratch
+    assert f(2, 0, P, P, P, P, P, P, P, P, 1, 15888, 128, 2048, 0, None) == 2
+    assert b"static scratch" in L.dg_last_error_message()
+    assert f(1, 0, P, P, P, P, P, P, P, P, 4, 16000, 128, 2048, 0, None) == 2  # contiguous rows too
+    assert f(2, 0, P, P, P, P, P, P, P, None, 4, 64, 256, 128, 0, None) == 1   # y missing
+    assert f(2, 0, P, P, P, P, Q, P, P, P, 4, 64, 256, 128, 0, None) == 3      # w2 misaligned
+    assert f(2, 0, P, P, P, P, P, P, P, P, 4, 64, 256, 100, 0, None) == 2      # I not a multiple of 128
+    assert f(2, 0, None, None, None, None, None, None, None, None, 0, 64, 256, 128, 0, None) == 0  # empty
+
+
 def test_convert_argument_errors(L):
     assert L.dg_convert_fp8_e4m3(P, 6, P, None) == 2   # not a multiple of 4
     assert L.dg_convert_fp8_e4m3(P, -4, P, None) == 1
