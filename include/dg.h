@@ -270,6 +270,17 @@ dg_status_t dg_moe_ffn_fp8_noalloc(int32_t layout, int32_t scale_fmt, const uint
  */
 dg_status_t dg_convert_fp8_e4m3(const float* x, int64_t n, uint8_t* q, void* stream);
 
+/*
+ * Re-reads the tuning switches from the environment. The library reads them once, at its first
+ * GEMM call; they only force a kernel schedule, never change what is computed, and are meant
+ * for tuning sessions and tests that compare schedules within one process:
+ *   DG_TILE=<name> (a tile kernel), DG_DECODE=v1 (the register-fed decode schedule),
+ *   DG_DECODE2="bn,kg,kpw,waves", DG_DECODE3="wave rows,wave columns,strips,slots" (one
+ *   decode configuration), DG_LOG (print each call's chosen kernel on stderr).
+ * Safe to call at any time; calls already enqueued are not affected.
+ */
+void dg_reload_tuning_switches(void);
+
 /* Human-readable name of a status code (static string). */
 const char* dg_status_string(dg_status_t status);
 

@@ -76,12 +76,20 @@ def lib() -> ctypes.CDLL:
         L.dg_moe_ffn_fp8_noalloc.restype = ctypes.c_int
         L.dg_convert_fp8_e4m3.argtypes = [P, I64, P, P]
         L.dg_convert_fp8_e4m3.restype = ctypes.c_int
+        L.dg_reload_tuning_switches.argtypes = []
+        L.dg_reload_tuning_switches.restype = None
         L.dg_status_string.argtypes = [ctypes.c_int]
         L.dg_status_string.restype = ctypes.c_char_p
         L.dg_last_error_message.argtypes = []
         L.dg_last_error_message.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def reload_tuning_switches() -> None:
+    """Makes the library re-read its DG_* tuning switches from the environment (it reads them
+    once per process otherwise)."""
+    lib().dg_reload_tuning_switches()
 
 
 def _check(status: int) -> None:

@@ -92,7 +92,7 @@ dg_status_t run_gemm(dg::Layout layout, int schedule, bool pow2, const uint8_t* 
   const char* chosen = "";
   hipError_t e = dg::launch_gemm(p, static_cast<dg::Schedule>(schedule), expected_m,
                                  static_cast<hipStream_t>(stream), &chosen);
-  if (getenv("DG_LOG")) fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
+  if (dg::log_switch()) fprintf(stderr, "[dg] %s M=%lld N=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
                                 (long long)N, (long long)K, (long long)G, chosen);
   return launched(e, name);
 }
@@ -159,7 +159,7 @@ dg_status_t run_swiglu(int32_t layout, int32_t scale_fmt, const uint8_t* a, cons
   p.M = M; p.N = 2 * I; p.K = K; p.G = (int32_t)G; p.layout = L; p.pow2 = scale_fmt == DG_SCALE_UE8M0;
   const char* chosen = "";
   const hipError_t e = dg::launch_gemm_swiglu(p, hq, sfh, expected_m, static_cast<hipStream_t>(stream), &chosen);
-  if (getenv("DG_LOG")) fprintf(stderr, "[dg] %s M=%lld I=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
+  if (dg::log_switch()) fprintf(stderr, "[dg] %s M=%lld I=%lld K=%lld G=%lld -> %s\n", name, (long long)M,
                                 (long long)I, (long long)K, (long long)G, chosen);
   if (e == hipErrorNotSupported) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: shape out of the kernel's range", name);
   return launched(e, name);
@@ -349,6 +349,8 @@ dg_status_t dg_moe_ffn_fp8_noalloc(int32_t layout, int32_t scale_fmt, const uint
   return run_gemm(L, 0, scale_fmt == DG_SCALE_UE8M0, hq, sfh, w2, sfw2, L == dg::Layout::Dense ? nullptr : meta, y,
                   L == dg::Layout::Dense ? 1 : G, M, H, I, expected_m, stream, name);
 }
+
+void dg_reload_tuning_switches(void) { dg::reload_tuning_switches(); }
 
 const char* dg_status_string(dg_status_t status) {
   switch (status) {

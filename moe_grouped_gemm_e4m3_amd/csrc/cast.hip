@@ -39,30 +39,57 @@ __device__ __forceinline__ uint32_t quant4(const float v[4], float s) {
   return packed;
 }
 
-// 32 lanes per 128-element chunk, 4 elements per lane; a 256-thread block covers 8
-// chunks per pass and walks the chunks grid-stride. Chunks are numbered in input order
-// (K block fastest), so the 8 chunks of a pass are 4 KB (fp32) of contiguous input; each
-// scale goes to its place in the K-block-major tensor [G][K/128][M]. Idx is uint32_t when
-// the chunk count fits.
-template <bool kBf16, bool kPow2, typename Idx>
-__global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x, Idx nchunks,
+// The codes of one chunk from its scale: q = e4m3(x / s) with the division correctly rounded
+// and the hardware conversion, which equals the saturating encoder for every |x / s| <= 464
+// (checked on every fp32 value). With s = fp32(amax / 448) >= amax / 448 * (1 - 2^-24), every
+// quotient is at most 448.00003; power-of-two scales are >= amax / 448. s == 0 (an all-zero
+// chunk, or amax / 448 underflowing) gives signed zeros.
+__device__ __forceinline__ uint32_t quant4_hw(const float v[4], float s) {
+  const uint32_t signs = ((__float_as_uint(v[0]) >> 31) << 7) | ((__float_as_uint(v[1]) >> 31) << 15) |
+                         ((__float_as_uint(v[2]) >> 31) << 23) | ((__float_as_uint(v[3]) >> 31) << 31);
+  const uint32_t codes = e4m3_hw_pack4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+  return s == 0.0f ? signs : codes;
+}
+
+// One wave per unit: a row (over the G*M rows) and a run of up to 2*P of its K blocks. Lanes
+// 0-31 take the even chunk of each pair, lanes 32-63 the odd one, 4 elements per lane, so a
+// load instruction covers 1 KB of contiguous input (fp32) and a unit's P loads are all issued
+// before its first reduction. The row's group, row and chunk offsets are computed once per
+// unit (integer divisions cost tens of VALU instructions, and this kernel is VALU-bound
+// otherwise). Units walk grid-stride; Idx is uint32_t when unit numbers stay below 2^32.
+template <bool kBf16, bool kPow2, typename Idx, int P>
+__global__ __launch_bounds__(256) void cast_per_token_kernel(const void* __restrict__ x, Idx nunits, Idx nseg,
                                                              Idx M, Idx kblocks, uint8_t* __restrict__ q,
                                                              float* __restrict__ sf) {
-  const int lane = threadIdx.x & 31;
-  const int64_t K = (int64_t)kblocks * kQ;
-  for (Idx c = (Idx)blockIdx.x * 8 + (Idx)(threadIdx.x >> 5); c < nchunks; c += (Idx)gridDim.x * 8) {
-    // chunk c in input order: row-major over (group, row), K block fastest
-    const Idx gr = c / kblocks, kb = c - gr * kblocks;
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  const Idx wave = (Idx)blockIdx.x * 4 + (Idx)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Idx nwaves = (Idx)gridDim.x * 4;
+  for (Idx u = wave; u < nunits; u += nwaves) {
+    const Idx gr = u / nseg, seg = u - gr * nseg;
     const Idx g = gr / M, r = gr - g * M;
-    const int64_t e0 = (int64_t)c * kQ + lane * 4;
-    float v[4];
-    load4<kBf16>(x, e0, v);
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    const int kb0 = (int)(seg * (Idx)(2 * P));
+    const int nk = min(2 * P, (int)kblocks - kb0);  // chunks of this unit
+    const int64_t e0 = ((int64_t)gr * (int64_t)kblocks + kb0 + half) * kQ + l32 * 4;
+    float v[P][4];
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-    const float s = kPow2 ? pow2_ceil(amax / 448.0f) : amax / 448.0f;
-    *reinterpret_cast<uint32_t*>(q + e0) = quant4(v, s);
-    if (lane == 0) sf[((int64_t)g * kblocks + kb) * M + r] = s;
+    for (int i = 0; i < P; ++i) {
+      v[i][0] = v[i][1] = v[i][2] = v[i][3] = 0.0f;
+      if (2 * i + half < nk) load4<kBf16>(x, e0 + (int64_t)(2 * i) * kQ, v[i]);
+    }
+    float* srow = sf + ((int64_t)g * (int64_t)kblocks + kb0 + half) * (int64_t)M + r;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      if (2 * i >= nk) break;  // wave-uniform
+      float amax = fmaxf(fmaxf(fabsf(v[i][0]), fabsf(v[i][1])), fmaxf(fabsf(v[i][2]), fabsf(v[i][3])));
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+      const float s = kPow2 ? pow2_ceil(amax / 448.0f) : amax / 448.0f;
+      const uint32_t packed = quant4_hw(v[i], s);
+      if (2 * i + half < nk) {
+        *reinterpret_cast<uint32_t*>(q + e0 + (int64_t)(2 * i) * kQ) = packed;
+        if (l32 == 0) srow[(int64_t)(2 * i) * (int64_t)M] = s;
+      }
+    }
   }
 }
 
@@ -110,21 +137,37 @@ __global__ __launch_bounds__(256) void convert_e4m3_kernel(const float4* __restr
   }
 }
 
+template <bool kPow2, typename Idx, int P>
+void launch_per_token(const void* x, int bf16, int64_t rows, int64_t M, int64_t kblocks, uint8_t* q, float* sf,
+                      hipStream_t stream) {
+  constexpr int64_t kMaxBlocks = 8192;  // grid-stride beyond ~32 blocks per CU
+  const int64_t nseg = (kblocks + 2 * P - 1) / (2 * P);
+  const int64_t nunits = rows * nseg;
+  int64_t blocks = (nunits + 3) / 4;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (bf16)
+    cast_per_token_kernel<true, kPow2, Idx, P><<<grid, block, 0, stream>>>(x, (Idx)nunits, (Idx)nseg, (Idx)M,
+                                                                            (Idx)kblocks, q, sf);
+  else
+    cast_per_token_kernel<false, kPow2, Idx, P><<<grid, block, 0, stream>>>(x, (Idx)nunits, (Idx)nseg, (Idx)M,
+                                                                             (Idx)kblocks, q, sf);
+}
+
 template <bool kPow2>
 hipError_t cast_per_token(const void* x, int bf16, int64_t G, int64_t M, int64_t K, uint8_t* q, float* sf,
                           hipStream_t stream) {
   const int64_t kblocks = K / kQ;
-  const int64_t nchunks = G * M * kblocks;
-  int64_t blocks = (nchunks + 7) / 8;
-  if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 blocks per CU
-  const dim3 grid((unsigned)blocks), block(256);
-  if (nchunks < ((int64_t)1 << 32) - 8 * 8192) {  // c + one grid stride stays below 2^32
-    const uint32_t n = (uint32_t)nchunks, m = (uint32_t)M, kbs = (uint32_t)kblocks;
-    if (bf16) cast_per_token_kernel<true, kPow2, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
-    else cast_per_token_kernel<false, kPow2, uint32_t><<<grid, block, 0, stream>>>(x, n, m, kbs, q, sf);
+  const int64_t rows = G * M;
+  // runs of 8 K blocks per wave once that still gives every CU about 32 waves; pairs keep
+  // small casts spread over more of the chip
+  const bool wide = rows * ((kblocks + 7) / 8) >= 256 * 32;
+  const bool small_idx = rows * kblocks < ((int64_t)1 << 32) - 4 * 8192 * 8;  // u + one stride < 2^32
+  if (small_idx) {
+    if (wide) launch_per_token<kPow2, uint32_t, 4>(x, bf16, rows, M, kblocks, q, sf, stream);
+    else launch_per_token<kPow2, uint32_t, 1>(x, bf16, rows, M, kblocks, q, sf, stream);
   } else {
-    if (bf16) cast_per_token_kernel<true, kPow2, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
-    else cast_per_token_kernel<false, kPow2, int64_t><<<grid, block, 0, stream>>>(x, nchunks, M, kblocks, q, sf);
+    launch_per_token<kPow2, int64_t, 4>(x, bf16, rows, M, kblocks, q, sf, stream);
   }
   return hipGetLastError();
 }

@@ -49,4 +49,10 @@ hipError_t launch_convert_e4m3(const float* x, uint8_t* q, int64_t n, hipStream_
 hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q, float* sf,
                                  hipStream_t stream);
 
+// The DG_* tuning switches (DG_TILE, DG_DECODE, DG_DECODE2, DG_DECODE3, DG_LOG) are read
+// from the environment once per process; this reads them again.
+void reload_tuning_switches();
+// DG_LOG is set: every call names its chosen kernel on stderr.
+bool log_switch();
+
 }  // namespace dg

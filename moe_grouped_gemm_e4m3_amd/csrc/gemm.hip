@@ -23,6 +23,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "dg_device.h"
 #include "dg_launch.h"
@@ -619,351 +620,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_decode3_kernel(KParams p) {
 }
 
 
-
-// ---------------------------------------------------------------------------------
-// decode schedule with the activation block resident in LDS
-// ---------------------------------------------------------------------------------
-// For M <= 64 and 64*K bytes that fit in LDS: a workgroup first copies its 64 x K
-// activation block (and its scales) into LDS once, with direct global->LDS loads, then
-// streams the weight columns of its share of the output. The column range is cut into
-// units of 16*TN columns; KSPLIT waves share a unit, each summing every KSPLIT-th K
-// block, and NW/KSPLIT units are in flight at once. Every weight byte is read once; the
-// activation block is read once per workgroup instead of once per column tile.
-// LDS: A as [K block][64 rows][128 bytes] with 16-byte chunks XOR-swizzled by row,
-// then the activation scales [K block][64 rows], then (KSPLIT-1) partial tiles per slot.
-template <int TN, int KSPLIT, int NW, int KW, Layout L>
-__global__ __launch_bounds__(64 * NW) void gemm_decode_lds_kernel(KParams p) {
-  static_assert(L != Layout::Contiguous, "decode schedule serves dense and masked layouts");
-  static_assert(NW % KSPLIT == 0, "waves split evenly over unit slots");
-  constexpr int SLOTS = NW / KSPLIT;
-  constexpr int UW = 16 * TN;  // columns per unit
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-
-  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
-  const int part = (int)(wg % (uint32_t)p.tiles_n);
-  const int mb = (int)((wg / (uint32_t)p.tiles_n) % (uint32_t)p.tiles_m);
-  const int g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
-  const int64_t m0 = (int64_t)mb * 64;
-  int64_t valid = p.M;
-  if constexpr (L == Layout::Masked) valid = clamp_rows(p.masked_m[g], p.M);
-  if (m0 >= valid) return;  // uniform over the workgroup
-  const int nkb = p.nkb;
-  const int64_t K = p.K;
-  const int units = (int)(p.N / UW);
-  const int u0 = (int)((int64_t)units * part / p.tiles_n);
-  const int u1 = (int)((int64_t)units * (part + 1) / p.tiles_n);
-
-  const uint8_t* A = p.a + (int64_t)g * p.M * K;
-  const float* SA = p.sfa + (int64_t)g * p.M * nkb;
-  const uint8_t* B = p.b + (int64_t)g * p.N * K;
-  const float* SBg = p.sfb + (int64_t)g * (p.N / kQ) * nkb;
-  uint16_t* D = p.d + (int64_t)g * p.M * p.N;
-
-  uint8_t* sA = smem;
-  float* sSa = reinterpret_cast<float*>(smem + 64 * K);
-  float* sRed = sSa + 64 * nkb;
-
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
-
-  // phase 1: A block and its scales into LDS, K-block-major: sA[kb][row][128 bytes]
-  // (16-byte chunks XOR-swizzled by row) and sSa[kb][row]. One direct-to-LDS instruction
-  // fills 1 KB (lane i -> bytes 16i..16i+15) = 8 rows of one K block; each lane fetches
-  // the global chunk that belongs at its LDS position.
-  {
-    const int nchunk = nkb * 512;  // 64 rows x 8 chunks per K block
-    for (int c0 = w * 64; c0 < nchunk; c0 += 64 * NW) {
-      const int c = c0 + l;
-      const int kb = c >> 9, row = (c >> 3) & 63, ch = c & 7;
-      const uint8_t* src = A + clamp_rows(m0 + row, valid - 1) * K + kb * kQ + ((ch ^ (row & 7)) << 4);
-      __builtin_amdgcn_global_load_lds(src, sA + (uint32_t)c0 * 16, 16, 0, 0);
-    }
-    for (int i = t; i < 64 * nkb; i += 64 * NW) {
-      const int kb = i >> 6, row = i & 63;
-      sSa[i] = SA[(int64_t)kb * p.M + clamp_rows(m0 + row, valid - 1)];
-    }
-  }
-
-  const int slot = w / KSPLIT, kpart = w % KSPLIT;
-  const int fr = l & 15;
-  const int g4 = l >> 4;
-  const int kof = g4 * 16;
-  // swizzled positions of this lane's two 16-byte chunks (g4 and g4+4) in its row
-  const int sw0 = (g4 ^ (fr & 7)) << 4, sw1 = ((g4 + 4) ^ (fr & 7)) << 4;
-
-  // all weight fragments of this wave's K blocks for the unit of round `ub`
-  auto issue = [&](v8i (&bf)[KW][TN], float (&sbv)[KW], int ub) {
-    const int u = min(ub + slot, u1 - 1);
-    const int64_t n0 = (int64_t)u * UW;
-    const uint8_t* bp = B + (n0 + fr) * K + kof;  // this lane's row of the unit
-    const float* SB = SBg + (n0 / kQ) * nkb;
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      const int kb = kpart + KSPLIT * i;
-      const int kc = min(kb, nkb - 1);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bf[i][j] = load_frag_global(bp + (uint32_t)(16 * j * (int)K + kc * kQ));
-      sbv[i] = SB[kc] * (kb < nkb ? 1.0f : 0.0f);
-    }
-  };
-
-  auto consume = [&](v8i (&bf)[KW][TN], float (&sbv)[KW], int ub) {
-    const int u = ub + slot;
-    const bool active = u < u1;
-    const int64_t n0 = (int64_t)min(u, u1 - 1) * UW;
-    v4f acc[4][TN];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      const int kb = kpart + KSPLIT * i;
-      const int kc = min(kb, nkb - 1);
-      const uint8_t* ablk = sA + kc * 8192 + fr * 128;
-      const float* sblk = sSa + kc * 64 + 4 * g4;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const v8i af = cat8(*reinterpret_cast<const v4i*>(ablk + s * 2048 + sw0),
-                            *reinterpret_cast<const v4i*>(ablk + s * 2048 + sw1));
-        const float4 s4 = *reinterpret_cast<const float4*>(sblk + 16 * s);
-        const float t0 = s4.x * sbv[i], t1 = s4.y * sbv[i], t2 = s4.z * sbv[i], t3 = s4.w * sbv[i];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const v4f pp = mfma_f8_16x16x128(af, bf[i][j]);
-          acc[s][j][0] = fmaf(pp[0], t0, acc[s][j][0]);
-          acc[s][j][1] = fmaf(pp[1], t1, acc[s][j][1]);
-          acc[s][j][2] = fmaf(pp[2], t2, acc[s][j][2]);
-          acc[s][j][3] = fmaf(pp[3], t3, acc[s][j][3]);
-        }
-      }
-      // keep the scheduler from hoisting every K block's LDS reads (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (KSPLIT > 1) {
-      // partial tiles of K parts 1.. go through LDS to the K-part-0 wave of the slot
-      if (kpart > 0) {
-        float* dst = sRed + ((slot * (KSPLIT - 1) + (kpart - 1)) * 64) * UW;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(16 * s + 4 * g4 + r) * UW + 16 * j + fr] = acc[s][j][r];
-      }
-      lds_barrier();
-      if (kpart == 0) {
-#pragma unroll
-        for (int q = 1; q < KSPLIT; ++q) {
-          const float* src = sRed + ((slot * (KSPLIT - 1) + (q - 1)) * 64) * UW;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[s][j][r] += src[(16 * s + 4 * g4 + r) * UW + 16 * j + fr];
-        }
-      }
-    }
-    if (kpart == 0 && active) {
-      uint16_t* dbase = D + (m0 + 4 * g4) * p.N + n0 + fr;
-      const int rows_left = (int)(valid - m0 - 4 * g4);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (16 * s + r < rows_left) {
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              dbase[(uint32_t)((16 * s + r) * (int)p.N + 16 * j)] = (uint16_t)bf16_rne(acc[s][j][r]);
-          }
-        }
-      }
-    }
-    if constexpr (KSPLIT > 1) lds_barrier();  // the partial slots are reused next round
-  };
-
-  if (u0 >= u1) {  // no columns for this workgroup: drain the LDS loads and leave
-    __builtin_amdgcn_s_waitcnt(0);
-    return;
-  }
-  // rounds of SLOTS units; the next round's weights load while this round computes
-  v8i bfa[KW][TN], bfb[KW][TN];
-  float sba[KW], sbb[KW];
-  issue(bfa, sba, u0);
-  __builtin_amdgcn_s_waitcnt(0);  // the A block (direct-to-LDS) has landed, in every wave
-  __syncthreads();
-  for (int ub = u0;;) {
-    if (ub + SLOTS >= u1) { consume(bfa, sba, ub); break; }
-    issue(bfb, sbb, ub + SLOTS);
-    consume(bfa, sba, ub);
-    ub += SLOTS;
-    if (ub + SLOTS >= u1) { consume(bfb, sbb, ub); break; }
-    issue(bfa, sba, ub + SLOTS);
-    consume(bfb, sbb, ub);
-    ub += SLOTS;
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// tile schedule
-// ---------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, Layout L>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tile_kernel(KParams p) {
-  constexpr int NT = 64 * WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int ACH = BM * 8 / NT;  // 16-byte chunks of an A K-block per thread
-  constexpr int BCH = BN * 8 / NT;
-  static_assert(ACH * NT == BM * 8 && BCH * NT == BN * 8, "chunk split");
-  static_assert(kQ % BN == 0, "tile must sit inside one weight-scale block column");
-  static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
-  static_assert(BM <= NT, "one activation scale per thread");
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kQ];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kQ];
-  __shared__ __attribute__((aligned(16))) float sSa[2][BM];
-
-  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
-  int g = 0, tm, tn;
-  if constexpr (L == Layout::Masked) {
-    // m-tiles of one (group, n-tile) are adjacent, so they meet the same B tile in L2
-    tm = (int)(wg % (uint32_t)p.tiles_m);
-    tn = (int)((wg / (uint32_t)p.tiles_m) % (uint32_t)p.tiles_n);
-    g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
-  } else {
-    // raster in bands of 8 m-tiles: n advances after each band column
-    constexpr int GM = 8;
-    const int per_band = GM * p.tiles_n;
-    const int band = (int)wg / per_band;
-    const int first = band * GM;
-    const int gm = min(p.tiles_m - first, GM);
-    const int in = (int)wg % per_band;
-    tm = first + in % gm;
-    tn = in / gm;
-  }
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  int64_t valid = p.M;
-  if constexpr (L == Layout::Masked) {
-    valid = clamp_rows(p.masked_m[g], p.M);
-    if (m0 >= valid) return;  // uniform over the workgroup
-  }
-  if constexpr (L == Layout::Contiguous) {
-    g = p.m_indices[m0];
-    if (g < 0 || g >= p.G) return;  // padding block (or an id outside the groups)
-  }
-  const int nkb = p.nkb;
-  const int64_t K = p.K;
-  const uint8_t* A = p.a + (L == Layout::Masked ? (int64_t)g * p.M * K : 0);
-  const float* SA = p.sfa + (L == Layout::Masked ? (int64_t)g * p.M * nkb : 0);
-  const uint8_t* B = p.b + (int64_t)g * p.N * K;
-  const float* SB = p.sfb + ((int64_t)g * (p.N / kQ) + n0 / kQ) * nkb;
-  uint16_t* D = p.d + (L == Layout::Masked ? (int64_t)g * p.M * p.N : 0);
-
-  const int t = threadIdx.x, w = t >> 6, l = t & 63;
-  const int wm = w % WM, wn = w / WM;
-
-  // global -> LDS staging assignment: chunk c = t + NT*u is row c/8, 16-byte column c%8
-  const uint8_t* ga[ACH];
-  uint32_t la[ACH];
-#pragma unroll
-  for (int u = 0; u < ACH; ++u) {
-    const int c = t + NT * u, row = c >> 3, ch = c & 7;
-    ga[u] = A + clamp_rows(m0 + row, valid - 1) * K + ch * 16;
-    la[u] = row * kQ + ((ch ^ (row & 7)) << 4);
-  }
-  const uint8_t* gb[BCH];
-  uint32_t lb[BCH];
-#pragma unroll
-  for (int u = 0; u < BCH; ++u) {
-    const int c = t + NT * u, row = c >> 3, ch = c & 7;
-    gb[u] = B + (n0 + row) * K + ch * 16;
-    lb[u] = row * kQ + ((ch ^ (row & 7)) << 4);
-  }
-  const float* gsa = SA + clamp_rows(m0 + (t < BM ? t : 0), valid - 1);  // + kb * M
-
-  v4i ra[ACH], rb[BCH];
-  float rsa = 0.f;
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < ACH; ++u) ra[u] = *reinterpret_cast<const v4i*>(ga[u] + (int64_t)kb * kQ);
-#pragma unroll
-    for (int u = 0; u < BCH; ++u) rb[u] = *reinterpret_cast<const v4i*>(gb[u] + (int64_t)kb * kQ);
-    if (t < BM) rsa = gsa[(int64_t)kb * p.M];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < ACH; ++u) *reinterpret_cast<v4i*>(&sA[buf][la[u]]) = ra[u];
-#pragma unroll
-    for (int u = 0; u < BCH; ++u) *reinterpret_cast<v4i*>(&sB[buf][lb[u]]) = rb[u];
-    if (t < BM) sSa[buf][t] = rsa;
-  };
-
-  v4f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // fragment read offsets: 16-byte columns (l>>4) and 4+(l>>4) of the row, swizzled
-  const int fr = l & 15;
-  const int c0 = l >> 4, c1 = c0 + 4;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  float sb = SB[0];
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    float sb_next = 0.f;
-    if (kb + 1 < nkb) {
-      gload(kb + 1);
-      sb_next = SB[kb + 1];
-    }
-    const uint8_t* a_s = sA[cur];
-    const uint8_t* b_s = sB[cur];
-    v8i bfr[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int row = wn * WTN + 16 * j + fr;
-      const uint8_t* base = b_s + row * kQ;
-      bfr[j] = cat8(*reinterpret_cast<const v4i*>(base + ((c0 ^ (row & 7)) << 4)),
-                    *reinterpret_cast<const v4i*>(base + ((c1 ^ (row & 7)) << 4)));
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int row = wm * WTM + 16 * i + fr;
-      const uint8_t* base = a_s + row * kQ;
-      const v8i afr = cat8(*reinterpret_cast<const v4i*>(base + ((c0 ^ (row & 7)) << 4)),
-                           *reinterpret_cast<const v4i*>(base + ((c1 ^ (row & 7)) << 4)));
-      const float4 s4 = *reinterpret_cast<const float4*>(&sSa[cur][wm * WTM + 16 * i + 4 * (l >> 4)]);
-      const float t0 = s4.x * sb, t1 = s4.y * sb, t2 = s4.z * sb, t3 = s4.w * sb;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4f pp = mfma_f8_16x16x128(afr, bfr[j]);
-        acc[i][j][0] = fmaf(pp[0], t0, acc[i][j][0]);
-        acc[i][j][1] = fmaf(pp[1], t1, acc[i][j][1]);
-        acc[i][j][2] = fmaf(pp[2], t2, acc[i][j][2]);
-        acc[i][j][3] = fmaf(pp[3], t3, acc[i][j][3]);
-      }
-    }
-    if (kb + 1 < nkb) lstore(cur ^ 1);
-    sb = sb_next;
-    __syncthreads();
-  }
-
-  // epilogue: bf16 round-to-nearest-even, rows beyond the valid count are not written
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm * WTM + 16 * i + 4 * (l >> 4) + r;
-      if (row < valid) {
-        uint16_t* drow = D + row * p.N + n0 + wn * WTN + fr;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) drow[16 * j] = (uint16_t)bf16_rne(acc[i][j][r]);
-      }
-    }
-  }
-}
 
 template <int BN, int NW, int KPW, Layout L>
 hipError_t run_decode(KParams kp, hipStream_t s) {
@@ -1795,16 +1451,59 @@ hipError_t run_tile3(KParams kp, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, Layout L>
-hipError_t run_tile(KParams kp, hipStream_t s) {
-  kp.tiles_n = (int)(kp.N / BN);
-  kp.tiles_m = (int)((kp.M + BM - 1) / BM);
-  const int64_t nwg = (int64_t)(L == Layout::Masked ? kp.G : 1) * kp.tiles_m * kp.tiles_n;
-  if (nwg <= 0) return hipSuccess;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  kp.nwg = (int)nwg;
-  gemm_tile_kernel<BM, BN, WM, WN, L><<<dim3((unsigned)nwg), dim3(64 * WM * WN), 0, s>>>(kp);
-  return hipGetLastError();
+// Tuning switches, read from the environment once per process (at the first GEMM call) and
+// again only on request (reload_tuning_switches):
+//   DG_TILE=<name>    forces one of the tile kernels where it applies (names in launch_gemm);
+//   DG_DECODE=v1      the register-fed decode schedule; any DG_DECODE value keeps dense M <= 64
+//                     on the decode schedules;
+//   DG_DECODE2=bn,kg,kpw,waves   one LDS decode configuration (set at all: not decode3);
+//   DG_DECODE3=wm,wn,strips,slots one activation-resident decode configuration;
+//   DG_LOG            names the chosen kernel of every call on stderr.
+struct Tuning {
+  char tile[32] = "";
+  bool decode_set = false, decode_v1 = false;
+  bool decode2_set = false, decode2_ok = false;
+  int decode2[4] = {0, 0, 0, 0};
+  bool decode3_ok = false;
+  int decode3[4] = {0, 0, 0, 0};
+  bool log = false;
+};
+
+Tuning read_tuning() {
+  Tuning t;
+  if (const char* v = getenv("DG_TILE")) snprintf(t.tile, sizeof t.tile, "%s", v);
+  if (const char* v = getenv("DG_DECODE")) {
+    t.decode_set = true;
+    t.decode_v1 = strcmp(v, "v1") == 0;
+  }
+  if (const char* v = getenv("DG_DECODE2")) {
+    t.decode2_set = true;
+    int* c = t.decode2;
+    t.decode2_ok = sscanf(v, "%d,%d,%d,%d", &c[0], &c[1], &c[2], &c[3]) == 4;
+  }
+  if (const char* v = getenv("DG_DECODE3")) {
+    int* c = t.decode3;
+    t.decode3_ok = sscanf(v, "%d,%d,%d,%d", &c[0], &c[1], &c[2], &c[3]) == 4;
+  }
+  t.log = getenv("DG_LOG") != nullptr;
+  return t;
+}
+
+std::mutex g_tuning_mu;
+std::atomic<const Tuning*> g_tuning{nullptr};
+
+// The current record. A reload publishes a new one and keeps the old one alive, since a launch
+// on another thread may still be reading it (a few dozen bytes per reload).
+const Tuning& tuning() {
+  const Tuning* t = g_tuning.load(std::memory_order_acquire);
+  if (t) return *t;
+  std::lock_guard<std::mutex> lock(g_tuning_mu);
+  t = g_tuning.load(std::memory_order_relaxed);
+  if (!t) {
+    t = new Tuning(read_tuning());
+    g_tuning.store(t, std::memory_order_release);
+  }
+  return *t;
 }
 
 constexpr size_t kLdsBytes = 163840;  // gfx950 LDS per workgroup
@@ -1823,94 +1522,10 @@ hipError_t allow_full_lds() {
   return e;
 }
 
-template <int TN, int KSPLIT, int NW, int KW>
-constexpr size_t decode_lds_bytes(int64_t K, int nkb) {
-  return (size_t)(64 * K) + (size_t)4 * 64 * nkb + (size_t)(NW / KSPLIT) * (KSPLIT - 1) * 64 * 16 * TN * 4;
-}
-
-template <int TN, int KSPLIT, int NW, int KW, Layout L>
-hipError_t run_decode_lds(KParams kp, int parts, hipStream_t s) {
-  const size_t lds = decode_lds_bytes<TN, KSPLIT, NW, KW>(kp.K, kp.nkb);
-  if (lds > kLdsBytes || (int64_t)KSPLIT * KW < kp.nkb || parts < 1) return hipErrorInvalidValue;
-  kp.tiles_m = (int)((kp.M + 63) / 64);
-  kp.tiles_n = parts;
-  const int64_t nwg = (int64_t)kp.G * kp.tiles_m * parts;
-  if (nwg <= 0) return hipSuccess;
-  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
-  kp.nwg = (int)nwg;
-  const hipError_t attr = allow_full_lds<&gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L>>();
-  if (attr != hipSuccess) return attr;
-  gemm_decode_lds_kernel<TN, KSPLIT, NW, KW, L><<<dim3((unsigned)nwg), dim3(64 * NW), lds, s>>>(kp);
-  return hipGetLastError();
-}
-
-// Instantiated configurations of the LDS-resident decode schedule:
-// (columns/16 per unit, waves per unit, waves, K blocks per wave).
-#define DG_DECODE_LDS_CONFIGS(X) \
-  X(1, 4, 8, 4) X(1, 4, 8, 3) X(1, 4, 8, 2) X(1, 2, 8, 4) X(1, 8, 8, 2) X(1, 2, 8, 2)
-
-struct DecodeLdsCfg { int tn, ksplit, nw, kw; };
-
-template <Layout L>
-hipError_t run_decode_lds_cfg(const DecodeLdsCfg& c, int parts, const KParams& kp, hipStream_t s, bool* found) {
-  *found = true;
-#define DG_X(a, b, c_, d) \
-  if (c.tn == a && c.ksplit == b && c.nw == c_ && c.kw == d) return run_decode_lds<a, b, c_, d, L>(kp, parts, s);
-  DG_DECODE_LDS_CONFIGS(DG_X)
-#undef DG_X
-  *found = false;
-  return hipSuccess;
-}
-
-size_t decode_lds_need(const DecodeLdsCfg& c, int64_t K, int nkb) {
-  return (size_t)(64 * K) + (size_t)4 * 64 * nkb + (size_t)(c.nw / c.ksplit) * (c.ksplit - 1) * 64 * 16 * c.tn * 4;
-}
-
-// Picks an LDS-resident decode configuration, or returns false when none fits.
-template <Layout L>
-bool try_decode_lds(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
-  static thread_local char name[80];
-  const int nkb = kp.nkb;
-  if (kp.N * 64 >= ((int64_t)1 << 31)) return false;  // 32-bit output offsets
-  DecodeLdsCfg c{0, 0, 0, 0};
-  int parts = 0;
-  const char* env = getenv("DG_DECODE_LDS");
-  if (env && sscanf(env, "%d,%d,%d,%d,%d", &c.tn, &c.ksplit, &c.nw, &c.kw, &parts) == 5) {
-    // tuning override
-  } else {
-    static const DecodeLdsCfg prefs[] = {{1, 2, 8, 2}, {1, 4, 8, 2}, {1, 2, 8, 4}, {1, 4, 8, 3}, {1, 4, 8, 4},
-                                         {1, 8, 8, 2}};
-    const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
-    bool got = false;
-    for (const DecodeLdsCfg& q : prefs) {
-      if ((int64_t)q.ksplit * q.kw < nkb || decode_lds_need(q, kp.K, nkb) > kLdsBytes) continue;
-      const int64_t units = kp.N / (16 * q.tn);
-      const int slots = q.nw / q.ksplit;
-      // at most one round per workgroup and enough workgroups to cover the CUs
-      const int64_t p1 = (units + slots - 1) / slots;
-      if (p1 * rowblocks < 200) continue;
-      c = q;
-      parts = (int)(p1 * rowblocks > 512 ? (512 + rowblocks - 1) / rowblocks : p1);
-      got = true;
-      break;
-    }
-    if (!got) return false;
-  }
-  if (decode_lds_need(c, kp.K, nkb) > kLdsBytes || (int64_t)c.ksplit * c.kw < nkb) return false;
-  bool found = false;
-  *err = run_decode_lds_cfg<L>(c, parts, kp, s, &found);
-  if (!found) return false;
-  snprintf(name, sizeof name, "decode_lds_tn%d_ks%d_w%d_kw%d_p%d", c.tn, c.ksplit, c.nw, c.kw, parts);
-  if (chosen) *chosen = name;
-  return true;
-}
-
-// Instantiated decode configurations: (columns per workgroup, waves, K blocks per wave
-// per round).
+// Instantiated configurations of the register-fed decode schedule, the ones its automatic
+// choice takes: (columns per workgroup, waves, K blocks per wave per round).
 #define DG_DECODE_CONFIGS(X) \
-  X(16, 8, 2) X(16, 4, 3) X(16, 4, 4) X(16, 6, 2) X(16, 12, 1) X(16, 8, 1) \
-  X(32, 4, 3) X(32, 8, 2) X(32, 4, 4) X(32, 6, 2) X(32, 12, 1) X(32, 8, 1) \
-  X(48, 4, 3) X(48, 6, 2) X(48, 8, 2) X(64, 8, 2) X(64, 4, 3) X(64, 4, 4)
+  X(48, 4, 3) X(32, 4, 3) X(32, 8, 2) X(32, 4, 4) X(16, 8, 2) X(16, 4, 3) X(16, 4, 4)
 
 template <Layout L>
 hipError_t run_decode_cfg(int bn, int nw, int kpw, const KParams& kp, hipStream_t s, bool* found) {
@@ -1988,8 +1603,9 @@ template <Layout L>
 bool try_decode3(const KParams& kp, hipStream_t s, const char** chosen, hipError_t* err) {
   static thread_local char name[48];
   int wm = 2, wn = 3, tn = 2, st = 4;
-  const char* env = getenv("DG_DECODE3");
-  if (env && sscanf(env, "%d,%d,%d,%d", &wm, &wn, &tn, &st) == 4) {
+  const Tuning& t = tuning();
+  if (t.decode3_ok) {
+    wm = t.decode3[0]; wn = t.decode3[1]; tn = t.decode3[2]; st = t.decode3[3];
   } else {
     const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
     if (kp.N % 96 != 0 || rowblocks * (kp.N / 96) < 240) return false;
@@ -2032,8 +1648,9 @@ bool try_decode2(const KParams& kp, hipStream_t s, const char** chosen, hipError
   };
   const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
   C c{0, 0, 0, 0};
-  const char* env = getenv("DG_DECODE2");  // tuning: "bn,kg,kpw,nw"
-  if (env && sscanf(env, "%d,%d,%d,%d", &c.bn, &c.kg, &c.kpw, &c.nw) == 4) {
+  const Tuning& t = tuning();
+  if (t.decode2_ok) {
+    c = C{t.decode2[0], t.decode2[1], t.decode2[2], t.decode2[3]};
   } else {
     int64_t best = 0;
     for (const C& q : cfgs) {
@@ -2056,48 +1673,30 @@ bool try_decode2(const KParams& kp, hipStream_t s, const char** chosen, hipError
 template <Layout L>
 hipError_t run_decode_auto(const KParams& kp, hipStream_t s, const char** chosen) {
   static thread_local char name[64];
-  const char* which = getenv("DG_DECODE");  // tuning: "v1" keeps the register-fed schedule
-  if (!(which && strcmp(which, "v1") == 0)) {
+  const Tuning& t = tuning();
+  if (!t.decode_v1) {
     hipError_t e = hipSuccess;
-    if (!getenv("DG_DECODE2") && try_decode3<L>(kp, s, chosen, &e)) return e;
+    if (!t.decode2_set && try_decode3<L>(kp, s, chosen, &e)) return e;
     if (try_decode2<L>(kp, s, chosen, &e)) return e;
   }
-  if (getenv("DG_DECODE_LDS")) {  // tuning: the LDS-resident variant
-    hipError_t e = hipSuccess;
-    if (try_decode_lds<L>(kp, s, chosen, &e)) return e;
+  // register-fed schedule: one round per wave (all K blocks of a wave in flight at once);
+  // among those, the first configuration (measured order: nkb 12 -> (48,4,3) or (32,4,3),
+  // nkb 16 -> (32,8,2)) whose workgroup count covers the CUs
+  struct C { int bn, nw, kpw; };
+  static const C prefs[] = {{48, 4, 3}, {32, 4, 3}, {32, 8, 2}, {32, 4, 4}, {16, 8, 2}, {16, 4, 3}, {16, 4, 4}};
+  const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
+  C c{0, 0, 0};
+  for (const C& q : prefs) {
+    if (q.nw * q.kpw < kp.nkb || kp.N % q.bn != 0) continue;
+    if (rowblocks * (kp.N / q.bn) < 200) continue;
+    c = q;
+    break;
   }
-  int bn = 32, nw = 8, kpw = 2;
-  // DG_DECODE_CFG="bn,nw,kpw" overrides the choice (tuning); unknown triples are ignored.
-  const char* env = getenv("DG_DECODE_CFG");
-  bool forced = false;
-  if (env && sscanf(env, "%d,%d,%d", &bn, &nw, &kpw) == 3) forced = true;
-  if (!forced) {
-    // One round per wave (all K blocks of a wave in flight at once); among those, the
-    // first configuration (measured order) whose workgroup count covers the CUs.
-    const int64_t rowblocks = (int64_t)kp.G * ((kp.M + 63) / 64);
-    const int nkb = kp.nkb;
-    struct C { int bn, nw, kpw; };
-    // measured on MI355X (rocprofv3): nkb 12 -> (48,4,3) or (32,4,3); nkb 16 -> (32,8,2)
-    static const C prefs[] = {{48, 4, 3}, {32, 4, 3}, {32, 8, 2}, {32, 4, 4}, {16, 8, 2}, {16, 4, 3}, {16, 4, 4}};
-    bool got = false;
-    for (const C& c : prefs) {
-      if (c.nw * c.kpw < nkb || kp.N % c.bn != 0) continue;
-      if (rowblocks * (kp.N / c.bn) < 200) continue;
-      bn = c.bn; nw = c.nw; kpw = c.kpw; got = true;
-      break;
-    }
-    if (!got) {
-      if (rowblocks * (kp.N / 32) >= 200) { bn = 32; nw = 8; kpw = 2; }
-      else { bn = 16; nw = 8; kpw = 2; }
-    }
-  }
+  if (c.bn == 0) c = rowblocks * (kp.N / 32) >= 200 ? C{32, 8, 2} : C{16, 8, 2};
   bool found = false;
-  hipError_t e = run_decode_cfg<L>(bn, nw, kpw, kp, s, &found);
-  if (!found) {
-    bn = 32; nw = 8; kpw = 2;
-    e = run_decode_cfg<L>(bn, nw, kpw, kp, s, &found);
-  }
-  snprintf(name, sizeof name, "decode_bn%d_w%d_k%d", bn, nw, kpw);
+  const hipError_t e = run_decode_cfg<L>(c.bn, c.nw, c.kpw, kp, s, &found);
+  if (!found) return hipErrorInvalidValue;  // every entry of prefs is instantiated
+  snprintf(name, sizeof name, "decode_bn%d_w%d_k%d", c.bn, c.nw, c.kpw);
   if (chosen) *chosen = name;
   return e;
 }
@@ -2118,8 +1717,8 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
     // 64x24576x1536), else the LDS decode schedule
     if (p.layout == Layout::Dense) {
       const bool d3 = p.N % 96 == 0 && p.N / 96 >= 240 && decode3_need(96, 4, kp.nkb) <= kLdsBytes;
-      sched = p.M <= 64 ? (!d3 && p.N % 128 == 0 && p.N / 128 >= 160 && !getenv("DG_DECODE") &&
-                                   !getenv("DG_DECODE2")
+      const Tuning& t = tuning();
+      sched = p.M <= 64 ? (!d3 && p.N % 128 == 0 && p.N / 128 >= 160 && !t.decode_set && !t.decode2_set
                                ? Schedule::Tile64
                                : Schedule::Decode)
                         : (p.M >= 512 ? Schedule::Tile256 : Schedule::Tile128);
@@ -2135,18 +1734,13 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
   if (p.layout == Layout::Contiguous && sched != Schedule::Tile128) sched = Schedule::Tile128;
 
   // DG_TILE=<name> forces one of the tile kernels below where it applies (for tuning and
-  // for tests that compare them); DG_TILE_V1=1 selects the single-stage tile kernel.
-  const char* force = getenv("DG_TILE");
-  const bool v1 = getenv("DG_TILE_V1") != nullptr;
+  // for tests that compare them)
+  const char* force = tuning().tile[0] ? tuning().tile : nullptr;
   auto is = [&](const char* name) { return force && strcmp(force, name) == 0; };
   auto pick = [&](const char* name) { if (chosen) *chosen = name; };
   switch (p.layout) {
     case Layout::Dense:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Dense>(kp, stream, chosen);
-      if (v1) {
-        pick("tile_v1_128x128");
-        return run_tile<128, 128, 2, 2, Layout::Dense>(kp, stream);
-      }
       if (is("t2_256x128")) {
         pick("tile2_256x128");
         return run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
@@ -2192,10 +1786,6 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       return run_tile2<128, 128, 2, 4, Layout::Dense>(kp, stream);
     case Layout::Masked:
       if (sched == Schedule::Decode) return run_decode_auto<Layout::Masked>(kp, stream, chosen);
-      if (v1) {
-        pick("tile_v1_128x128");
-        return run_tile<128, 128, 2, 2, Layout::Masked>(kp, stream);
-      }
       if (sched == Schedule::Tile256) {
         if (is("t2_256x128")) {
           pick("tile2_256x128");
@@ -2230,10 +1820,6 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Masked>(kp, stream);
     case Layout::Contiguous:
-      if (v1) {
-        pick("tile_v1_128x128");
-        return run_tile<128, 128, 2, 2, Layout::Contiguous>(kp, stream);
-      }
       // the three-stage direct-load ring pays off once K is long enough to fill it (measured:
       // 8% faster than the register-staged kernel at K = 2048)
       if (is("t3_128x256b")) {
@@ -2263,7 +1849,7 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
   kp.m_indices = p.m_indices; kp.masked_m = p.masked_m;
   kp.M = p.M; kp.N = p.N; kp.K = p.K; kp.nkb = (int)(p.K / kQ); kp.G = p.G; kp.pow2 = p.pow2;
   kp.hq = hq; kp.sh = sh;
-  const char* force = getenv("DG_TILE");
+  const char* force = tuning().tile[0] ? tuning().tile : nullptr;
   auto is = [&](const char* name) { return force && strcmp(force, name) == 0; };
   auto pick = [&](const char* name) { if (chosen) *chosen = name; };
   switch (p.layout) {
@@ -2292,5 +1878,12 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
   }
   return hipErrorInvalidValue;
 }
+
+void reload_tuning_switches() {
+  std::lock_guard<std::mutex> lock(g_tuning_mu);
+  g_tuning.store(new Tuning(read_tuning()), std::memory_order_release);
+}
+
+bool log_switch() { return tuning().log; }
 
 }  // namespace dg

@@ -177,6 +177,19 @@ def test_hw_conversion_exhaustive(dg):
     assert total == 2 * (FP32_464 + 1)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_cast_wide_grid_bit_exact(dg, dtype):
+    # enough chunks (3 x 705 x 4224 / 128 = 69795) for the four-chunks-per-half-wave grid, with a
+    # ragged last pass; three groups so the scales land in the masked layout
+    x = synth.with_outliers(synth.normal((3, 705, 4224), 11, synth.TID_A), 11)
+    xt = torch.from_numpy(x).to(dtype)
+    say("cast wide grid 3x705x4224 %s" % dtype)
+    q, s = dg.cast_fp8_per_token(xt.to("cuda:0"))
+    qo, so = oracle.cast_per_token(xt.float().numpy().reshape(-1, 4224))
+    assert_same_bytes(q.view(-1, 4224), qo, "wide q")
+    assert_same_bits(s, kmajor(so.reshape(3, 705, 4224 // 128)), "wide s")
+
+
 def test_cast_bf16_input(dg):
     x = synth.with_outliers(synth.normal((40, 768), 8, synth.TID_A), 8)
     xb = torch.from_numpy(x).to(torch.bfloat16)

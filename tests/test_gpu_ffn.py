@@ -162,7 +162,7 @@ def test_ffn_masked(dg, pow2, expected_m):
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "masked"])
-def test_swiglu_split_issue_is_bitwise_the_same(dg, monkeypatch, layout):
+def test_swiglu_split_issue_is_bitwise_the_same(dg, switches, layout):
     # the fused gate/up kernel with the split issue (DG_TILE=t3_128x256b) sums the K blocks
     # exactly as the default 128x256 kernel: same hq bytes, same scales
     if layout == "contiguous":
@@ -174,9 +174,9 @@ def test_swiglu_split_issue_is_bitwise_the_same(dg, monkeypatch, layout):
         xq_d, sx_d, w1_d, s1_d, _, _, mm_d = dev
         run = lambda: dg.gemm_fp8_swiglu(MASKED, xq_d, sx_d, w1_d, s1_d, mm_d, expected_m=32)
     say("swiglu split issue %s" % layout)
-    monkeypatch.delenv("DG_TILE", raising=False)
+    switches.delenv("DG_TILE", raising=False)
     hq1, sh1 = run()
-    monkeypatch.setenv("DG_TILE", "t3_128x256b")
+    switches.setenv("DG_TILE", "t3_128x256b")
     hq2, sh2 = run()
     torch.cuda.synchronize()
     if layout == "masked":  # rows beyond the counts are not written: compare the valid ones

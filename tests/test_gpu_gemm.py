@@ -57,7 +57,7 @@ def test_long_k_fallbacks(dg, sched):
 
 
 @pytest.mark.parametrize("N,K", [(7168, 2048), (24576, 1536)])
-def test_decode_full_size(dg, monkeypatch, N, K):
+def test_decode_full_size(dg, switches, N, K):
     # the decode configurations, M = 64, in full against the whole oracle result
     say("dense decode full M=64 N=%d K=%d" % (N, K))
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, 64, N, K, seed=0)
@@ -69,11 +69,11 @@ def test_decode_full_size(dg, monkeypatch, N, K):
         assert_close(bf16_values(d2), R, "decode %dx%d %s" % (N, K, sched))
     # the activation-resident decode kernel and the 64x128 tile kernel sum the K blocks in
     # the same order with the same operations: bit for bit the same output
-    monkeypatch.setenv("DG_TILE", "t3_64x128")
+    switches.setenv("DG_TILE", "t3_64x128")
     d3 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
-    monkeypatch.setenv("DG_TILE", "d3_96")
+    switches.setenv("DG_TILE", "d3_96")
     d4 = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
-    monkeypatch.delenv("DG_TILE")
+    switches.delenv("DG_TILE")
     assert_close(bf16_values(d3), R, "decode %dx%d tile3 64x128" % (N, K))
     assert torch.equal(d3.view(torch.int16), d4.view(torch.int16))
 
@@ -184,15 +184,15 @@ TILE_VARIANTS = [None, "t2_128x128", "t2_256x128", "t3_256x128", "t3_128x256", "
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 1280), (512, 256, 2304), (77, 768, 384), (1000, 640, 640),
                                    (256, 256, 128)])
-def test_tile_kernels_parity_and_agreement(dg, monkeypatch, M, N, K):
+def test_tile_kernels_parity_and_agreement(dg, switches, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 3)
     R = oracle.gemm(oqa, osa, oqb, osb)
     ref = None
     for v in TILE_VARIANTS:
         if v:
-            monkeypatch.setenv("DG_TILE", v)
+            switches.setenv("DG_TILE", v)
         else:
-            monkeypatch.delenv("DG_TILE", raising=False)
+            switches.delenv("DG_TILE", raising=False)
         say("dense tile kernel %s M=%d N=%d K=%d" % (v, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["tile256"])
         assert_close(bf16_values(d), R, "tile %s" % v)
@@ -216,13 +216,13 @@ DECODE_VARIANTS = [("DG_DECODE", "v1"), ("DG_DECODE2", "96,4,3,8"), ("DG_DECODE2
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 1536, 1536), (37, 768, 2048), (1, 384, 1152), (130, 768, 1024)])
-def test_decode_variants(dg, monkeypatch, M, N, K):
+def test_decode_variants(dg, switches, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 11)
     R = oracle.gemm(oqa, osa, oqb, osb)
     for var, val in DECODE_VARIANTS:
         for v in ("DG_DECODE", "DG_DECODE2", "DG_DECODE3"):
-            monkeypatch.delenv(v, raising=False)
-        monkeypatch.setenv(var, val)
+            switches.delenv(v, raising=False)
+        switches.setenv(var, val)
         say("decode %s=%s M=%d N=%d K=%d" % (var, val, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=SCHEDULES["decode"])
         assert_close(bf16_values(d), R, "decode %s" % val)

@@ -62,21 +62,21 @@ def test_contiguous_parity(dg, G, tokens, N, K):
 
 
 @pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None, "t3_128x256b"])
-def test_contiguous_tile_kernels(dg, monkeypatch, variant):
+def test_contiguous_tile_kernels(dg, switches, variant):
     # long enough K for the automatic choice to take the direct-load ring; each kernel checked
     # against the oracle and against the others bit for bit
     G, N, K = 3, 512, 4352
     (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 300, N, K, seed=21)
     if variant:
-        monkeypatch.setenv("DG_TILE", variant)
+        switches.setenv("DG_TILE", variant)
     else:
-        monkeypatch.delenv("DG_TILE", raising=False)
+        switches.delenv("DG_TILE", raising=False)
     say("contiguous tile kernel %s" % variant)
     d = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
     R = oracle.grouped_contiguous(oqa, osa, oqb, osb, omi)
     valid = omi[:, None].repeat(N, 1) >= 0
     assert_close(bf16_values(d), R, "contiguous %s" % variant, mask=valid)
-    monkeypatch.setenv("DG_TILE", "t2_128x256")
+    switches.setenv("DG_TILE", "t2_128x256")
     d2 = dg.grouped_gemm_contiguous(qa, sa, qb, sb, mi)
     rows = torch.from_numpy(np.nonzero(omi >= 0)[0]).to("cuda:0")
     assert torch.equal(d[rows].view(torch.int16), d2[rows].view(torch.int16))
@@ -154,11 +154,11 @@ def test_masked_parity_and_sentinels(dg, sched):
 
 
 @pytest.mark.parametrize("variant", ["t3_256x256", "t3_128x256", "t2_256x128", "t3_256x256b", "t3_128x256b"])
-def test_masked_tile_kernels(dg, monkeypatch, variant):
+def test_masked_tile_kernels(dg, switches, variant):
     G, M_max, N, K = 5, 300, 512, 768
     mm = [0, 17, 128, 257, 300]
     (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 22, mm)
-    monkeypatch.setenv("DG_TILE", variant)
+    switches.setenv("DG_TILE", variant)
     d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("masked tile kernel %s" % variant)
     dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["tile256"])
@@ -167,14 +167,14 @@ def test_masked_tile_kernels(dg, monkeypatch, variant):
     assert_close(bf16_values(d), R, "masked %s" % variant, mask=valid)
     bits = d.view(torch.int16).cpu().numpy()
     assert (bits[~valid] == SENTINEL).all(), "rows beyond masked_m were written"
-    monkeypatch.delenv("DG_TILE")
+    switches.delenv("DG_TILE")
     d2 = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d2, schedule=MASKED_SCHEDULES["tile256"])
     assert torch.equal(d.view(torch.int16), d2.view(torch.int16))
 
 
 @pytest.mark.parametrize("cfg", ["2,3,2,4", "1,6,1,4", "2,2,3,5", "1,8,1,3"])
-def test_masked_activation_resident_decode(dg, monkeypatch, cfg):
+def test_masked_activation_resident_decode(dg, switches, cfg):
     # the activation-resident decode kernel on the masked layout, forced through DG_DECODE3
     # (decode schedule): empty, partial, full and multi-row-block groups, NaN codes in the
     # invalid activation rows, sentinels beyond the valid rows
@@ -186,7 +186,7 @@ def test_masked_activation_resident_decode(dg, monkeypatch, cfg):
     for g in range(G):
         qa[g, mm[g]:] = 0x7F
         oqa_nan[g, mm[g]:] = 0x7F
-    monkeypatch.setenv("DG_DECODE3", cfg)
+    switches.setenv("DG_DECODE3", cfg)
     d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("masked decode3 %s G=%d M_max=%d N=%d K=%d" % (cfg, G, M_max, N, K))
     dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d, schedule=MASKED_SCHEDULES["decode"])
@@ -214,10 +214,10 @@ def test_masked_split_issue_short_k(dg, K):
 
 
 @pytest.mark.parametrize("K", [128, 256, 384, 512])
-def test_split_issue_three_stages_short_k(dg, monkeypatch, K):
+def test_split_issue_three_stages_short_k(dg, switches, K):
     # the 128x256 tiles with the split issue (three stages: weights of K block kb+3 issued at
     # the start of K block kb) with 1 to 4 K blocks, on both grouped layouts
-    monkeypatch.setenv("DG_TILE", "t3_128x256b")
+    switches.setenv("DG_TILE", "t3_128x256b")
     G, N = 3, 512
     (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 200, N, K, seed=50 + K)
     say("contiguous split issue N=%d K=%d" % (N, K))

@@ -49,14 +49,14 @@ TILES = [None, "t3_256x128", "t3_128x256", "t2_256x128", "t2_128x128", "t3_256x2
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 2304), (300, 768, 1280), (77, 256, 384), (256, 256, 128)])
-def test_dense_ue8m0_tile_kernels(dg, monkeypatch, M, N, K):
+def test_dense_ue8m0_tile_kernels(dg, switches, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 1, outliers=True, ue8m0=True)
     R = oracle.gemm(oqa, osa, oqb, osb)
     for v in TILES:
         if v:
-            monkeypatch.setenv("DG_TILE", v)
+            switches.setenv("DG_TILE", v)
         else:
-            monkeypatch.delenv("DG_TILE", raising=False)
+            switches.delenv("DG_TILE", raising=False)
         say("dense ue8m0 tile %s M=%d N=%d K=%d" % (v, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=3, ue8m0=True)
         assert_close(bf16_values(d), R, "ue8m0 tile %s" % v)
@@ -70,14 +70,14 @@ DECODE = [(None, None), ("DG_DECODE2", "96,4,3,8"), ("DG_DECODE2", "96,1,12,6"),
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 1536, 1536), (37, 768, 2048), (130, 384, 1152)])
-def test_dense_ue8m0_decode(dg, monkeypatch, M, N, K):
+def test_dense_ue8m0_decode(dg, switches, M, N, K):
     (qa, sa, qb, sb), (oqa, osa, oqb, osb) = quantised_dense(dg, M, N, K, seed=M + 2, ue8m0=True)
     R = oracle.gemm(oqa, osa, oqb, osb)
     for var, v in DECODE:
-        monkeypatch.delenv("DG_DECODE2", raising=False)
-        monkeypatch.delenv("DG_DECODE3", raising=False)
+        switches.delenv("DG_DECODE2", raising=False)
+        switches.delenv("DG_DECODE3", raising=False)
         if var:
-            monkeypatch.setenv(var, v)
+            switches.setenv(var, v)
         say("dense ue8m0 decode %s=%s M=%d N=%d K=%d" % (var, v, M, N, K))
         d = dg.gemm_fp8_nt(qa, sa, qb, sb, schedule=1, ue8m0=True)
         assert_close(bf16_values(d), R, "ue8m0 decode %s" % v)
@@ -97,7 +97,7 @@ def test_ue8m0_power_of_two_invariance_is_bitwise(dg, sched):
     assert torch.equal((d1.float() * 0.25).view(torch.int32), d3.float().view(torch.int32))
 
 
-def test_contiguous_ue8m0(dg, monkeypatch):
+def test_contiguous_ue8m0(dg, switches):
     G, N, K = 3, 512, 4352
     a, b, mi = synth.contiguous_inputs(G, 300, N, K, 23)
     qa, sa = gpu_cast_tokens(dg, a, ue8m0=True)
@@ -110,7 +110,7 @@ def test_contiguous_ue8m0(dg, monkeypatch):
     R = oracle.grouped_contiguous(oqa, osa, oqb, osb, mi)
     valid = mi[:, None].repeat(N, 1) >= 0
     for v in ("t3_128x256", "t2_128x128"):
-        monkeypatch.setenv("DG_TILE", v)
+        switches.setenv("DG_TILE", v)
         say("contiguous ue8m0 %s" % v)
         d = dg.grouped_gemm_contiguous(qa, sa, qb, sb, to_dev(mi), ue8m0=True)
         assert_close(bf16_values(d), R, "contiguous ue8m0 %s" % v, mask=valid)
@@ -120,7 +120,7 @@ def test_contiguous_ue8m0(dg, monkeypatch):
 # kernel forced through DG_DECODE3 (decode schedule)
 @pytest.mark.parametrize("sched,tile", [(1, None), (3, None), (3, "t3_128x256"), (2, None), (1, "d3:1,8,1,3"),
                                         (1, "d3:2,4,1,3")])
-def test_masked_ue8m0_parity_and_sentinels(dg, monkeypatch, sched, tile):
+def test_masked_ue8m0_parity_and_sentinels(dg, switches, sched, tile):
     G, M_max, N, K = 5, 300, 512, 768
     mm = np.array([0, 17, 128, 257, 300], np.int32)
     a, b, _ = synth.masked_inputs(G, M_max, N, K, 24)
@@ -130,9 +130,9 @@ def test_masked_ue8m0_parity_and_sentinels(dg, monkeypatch, sched, tile):
     oqb, osb = oracle.cast_per_block(b, pow2=True)
     R = oracle.grouped_masked(oqa.reshape(G, M_max, K), osa.reshape(G, M_max, K // 128), oqb, osb, mm)
     if tile and tile.startswith("d3:"):
-        monkeypatch.setenv("DG_DECODE3", tile[3:])
+        switches.setenv("DG_DECODE3", tile[3:])
     elif tile:
-        monkeypatch.setenv("DG_TILE", tile)
+        switches.setenv("DG_TILE", tile)
     d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
     say("masked ue8m0 schedule %d tile %s" % (sched, tile))
     dg.grouped_gemm_masked(qa, sa, qb, sb, to_dev(mm), d=d, schedule=sched, ue8m0=True)
