@@ -1064,8 +1064,9 @@ __device__ __forceinline__ void swiglu_epilogue(const KParams& p, v4f (&acc)[TM]
 // The weights of K block kb+STAGES are then issued at the start of K block kb and its
 // activations after the middle barrier, so that half a K block more of loads is in flight,
 // for a second barrier per K block.
-template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2, bool kSwiglu = false, bool kSplit = false>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2, bool kSwiglu, bool kSplit>
+__device__ __forceinline__ void tile3_main(const KParams& p, uint8_t* smem, float (*sSB)[kMaxKb3], int g, int tm,
+                                           int tn) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -1078,7 +1079,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert(ADMA * 64 * NW == BM * 8 && BDMA * 64 * NW == BN * 8, "direct-load split");
   static_assert(SROWS >= 1 && SROWS <= 64 && SROWS * NW == BM, "scale rows per wave");
   static_assert((BN % kQ == 0 || kQ % BN == 0) && kQ % WTN == 0, "tile vs weight-scale blocks");
-  static_assert(L != Layout::Contiguous || BM == kQ, "contiguous layout: one expert per M tile");
+  // contiguous layout: one expert per row tile; a 256-row tile is launched only over two
+  // 128-row blocks of the same expert (gemm_contiguous_hybrid_kernel checks that)
+  static_assert(L != Layout::Contiguous || BM == kQ || BM == 2 * kQ, "contiguous layout: one expert per M tile");
   static_assert(TM >= 2 && TM % 2 == 0, "strip slots alternate and repeat every K block");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 1) * PER_STAGE < 64, "LDS ring depth");
   static_assert(!kSplit || (STAGES - 2) * PER_STAGE + BDMA < 64, "split issue: loads in flight");
@@ -1087,25 +1090,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   static_assert(!kSwiglu || (32 * (BM + 4) * 4 + BM * 8 + BM * (int)kQ <= STAGES * STAGE_BYTES &&
                              BM * BN * 2 <= STAGES * STAGE_BYTES),
                 "SwiGLU epilogue fits in the LDS ring");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float sSB[NB][kMaxKb3];  // this tile's weight scales
-
-  const uint32_t wg = xcd_remap(blockIdx.x, (uint32_t)p.nwg);
-  int g = 0, tm, tn;
-  if constexpr (L == Layout::Masked) {
-    tm = (int)(wg % (uint32_t)p.tiles_m);
-    tn = (int)((wg / (uint32_t)p.tiles_m) % (uint32_t)p.tiles_n);
-    g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
-  } else {
-    constexpr int GM = 8;
-    const int per_band = GM * p.tiles_n;
-    const int band = (int)wg / per_band;
-    const int first = band * GM;
-    const int gm = min(p.tiles_m - first, GM);
-    const int in = (int)wg % per_band;
-    tm = first + in % gm;
-    tn = in / gm;
-  }
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   int64_t valid = p.M;
   if constexpr (L == Layout::Masked) {
@@ -1419,6 +1403,88 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
   }
 }
 
+// Logical workgroup -> tile. Masked: row tile fastest, then column tile, then group. Other
+// layouts: bands of GM row tiles walked column by column, so neighbouring workgroups share
+// weight columns (and, under the XCD remap, one L2).
+__device__ __forceinline__ void tile_of(const KParams& p, uint32_t wg, bool masked, int& g, int& tm, int& tn,
+                                        int GM = 8) {
+  g = 0;
+  if (masked) {
+    tm = (int)(wg % (uint32_t)p.tiles_m);
+    tn = (int)((wg / (uint32_t)p.tiles_m) % (uint32_t)p.tiles_n);
+    g = (int)(wg / (uint32_t)(p.tiles_m * p.tiles_n));
+  } else {
+    const int per_band = GM * p.tiles_n;
+    const int band = (int)wg / per_band;
+    const int first = band * GM;
+    const int gm = min(p.tiles_m - first, GM);
+    const int in = (int)wg % per_band;
+    tm = first + in % gm;
+    tn = in / gm;
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, Layout L, bool kPow2, bool kSwiglu = false, bool kSplit = false>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tile3_kernel(KParams p) {
+  constexpr int NB = BN > (int)kQ ? BN / (int)kQ : 1;
+  constexpr int STAGE_BYTES = (BM + BN) * (int)kQ + BM * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float sSB[NB][kMaxKb3];  // this tile's weight scales
+  int g, tm, tn;
+  tile_of(p, xcd_remap(blockIdx.x, (uint32_t)p.nwg), L == Layout::Masked, g, tm, tn);
+  tile3_main<BM, BN, WM, WN, STAGES, L, kPow2, kSwiglu, kSplit>(p, smem, sSB, g, tm, tn);
+}
+
+// Masked layout, 256-row tiles: a tile with at most 128 valid rows (its group's count
+// minus its first row) runs as a 128 x 256 tile with three LDS stages (two K blocks of
+// weights in flight), a fuller one as a 256 x 256 tile with two stages and the split issue.
+// Each tile streams its group's weight columns once either way; the smaller row tile only
+// leaves LDS room for the third stage. Both bodies share one LDS allocation, and sum the K
+// blocks with the same operations as every other tile kernel.
+template <bool kPow2, bool kSwiglu>
+__global__ __launch_bounds__(512) void gemm_masked_hybrid_kernel(KParams p) {
+  constexpr int kSmallStage = (128 + 256) * (int)kQ + 128 * 4, kLargeStage = (256 + 256) * (int)kQ + 256 * 4;
+  constexpr int kBytes = 3 * kSmallStage > 2 * kLargeStage ? 3 * kSmallStage : 2 * kLargeStage;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBytes];
+  __shared__ __attribute__((aligned(16))) float sSB[2][kMaxKb3];
+  int g, tm, tn;
+  tile_of(p, xcd_remap(blockIdx.x, (uint32_t)p.nwg), true, g, tm, tn);  // tm counts 256-row tiles
+  const int64_t left = clamp_rows(p.masked_m[g], p.M) - (int64_t)tm * 256;
+  if (left <= 128)  // also the tiles with no valid row: the body returns at once
+    tile3_main<128, 256, 2, 4, 3, Layout::Masked, kPow2, kSwiglu, false>(p, smem, sSB, g, 2 * tm, tn);
+  else
+    tile3_main<256, 256, 2, 4, 2, Layout::Masked, kPow2, kSwiglu, true>(p, smem, sSB, g, tm, tn);
+}
+
+// Contiguous layout, 256-row tiles over pairs of 128-row blocks: a pair whose two blocks
+// belong to the same expert (the expert of each block's first row) runs as one 256 x 256
+// tile (two LDS stages, 1.5x fewer operand bytes per MFMA than 128 x 256); any other pair
+// runs as its two 128 x 256 blocks one after the other (three stages each; a block whose first
+// row is -1 is skipped as always). Bands of 4 row tiles (about one expert's rows at 8 experts
+// and 8192 tokens) walked column by column: the 32 workgroups an XCD takes in one round are
+// 4 row tiles x 8 column tiles, so each weight column tile is read by 4 of them and each
+// activation row tile by 8.
+template <bool kPow2, bool kSwiglu>
+__global__ __launch_bounds__(512) void gemm_contiguous_hybrid_kernel(KParams p) {
+  constexpr int kSmallStage = (128 + 256) * (int)kQ + 128 * 4, kLargeStage = (256 + 256) * (int)kQ + 256 * 4;
+  constexpr int kBytes = 3 * kSmallStage > 2 * kLargeStage ? 3 * kSmallStage : 2 * kLargeStage;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kBytes];
+  __shared__ __attribute__((aligned(16))) float sSB[2][kMaxKb3];
+  int g, tm, tn;
+  tile_of(p, xcd_remap(blockIdx.x, (uint32_t)p.nwg), false, g, tm, tn, 4);  // tm counts 256-row tiles
+  const int64_t r0 = (int64_t)tm * 256;
+  const int e0 = p.m_indices[r0];
+  const int e1 = r0 + 128 < p.M ? p.m_indices[r0 + 128] : -1;
+  if (e0 >= 0 && e0 < p.G && e1 == e0) {
+    tile3_main<256, 256, 2, 4, 2, Layout::Contiguous, kPow2, kSwiglu, false>(p, smem, sSB, 0, tm, tn);
+    return;
+  }
+  tile3_main<128, 256, 2, 4, 3, Layout::Contiguous, kPow2, kSwiglu, false>(p, smem, sSB, 0, 2 * tm, tn);
+  if (r0 + 128 >= p.M) return;
+  __syncthreads();  // every wave is done with the first block's LDS stages
+  tile3_main<128, 256, 2, 4, 3, Layout::Contiguous, kPow2, kSwiglu, false>(p, smem, sSB, 0, 2 * tm + 1, tn);
+}
+
 template <int BM, int BN, int WM, int WN, Layout L>
 hipError_t run_tile2(KParams kp, hipStream_t s) {
   kp.tiles_n = (int)(kp.N / BN);
@@ -1504,6 +1570,70 @@ const Tuning& tuning() {
     g_tuning.store(t, std::memory_order_release);
   }
   return *t;
+}
+
+// the masked hybrid of 128- and 256-row tiles; hipErrorNotSupported where run_tile3 would
+// refuse either body
+template <bool kSwiglu>
+hipError_t run_masked_hybrid(KParams kp, hipStream_t s) {
+  if (kp.N % 256 != 0 || kp.nkb > kMaxKb3 || kp.M * kp.K >= ((int64_t)1 << 32) ||
+      kp.N * kp.K >= ((int64_t)1 << 32) || kp.M * kp.nkb * 4 >= ((int64_t)1 << 32))
+    return hipErrorNotSupported;
+  kp.tiles_n = (int)(kp.N / 256);
+  kp.tiles_m = (int)((kp.M + 255) / 256);
+  const int64_t nwg = (int64_t)kp.G * kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  if (kp.pow2)
+    gemm_masked_hybrid_kernel<true, kSwiglu><<<dim3((unsigned)nwg), dim3(512), 0, s>>>(kp);
+  else
+    gemm_masked_hybrid_kernel<false, kSwiglu><<<dim3((unsigned)nwg), dim3(512), 0, s>>>(kp);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device; 256 on MI355X).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// The contiguous hybrid pays off when its rounds of 256-row tiles, each worth two 128-row
+// tiles, take no longer than the rounds of 128-row tiles: measured on 8 experts x 8192
+// tokens, 160 against 169 us at N = 7168, K = 2048 (8 rounds either way), but 340 against
+// 305 us at N = 4096, K = 7168 (544 tiles: 3 rounds of double tiles against 4.25 rounds).
+bool contiguous_hybrid_pays(const KParams& kp) {
+  const int64_t cus = cu_count();
+  const int64_t tn = kp.N / 256;
+  const int64_t t256 = ((kp.M + 255) / 256) * tn, t128 = (kp.M / 128) * tn;
+  return 2 * ((t256 + cus - 1) / cus) <= (t128 + cus - 1) / cus;
+}
+
+template <bool kSwiglu>
+hipError_t run_contiguous_hybrid(KParams kp, hipStream_t s) {
+  if (kp.N % 256 != 0 || kp.M % 128 != 0 || kp.nkb > kMaxKb3 || kp.M * kp.K >= ((int64_t)1 << 32) ||
+      kp.N * kp.K >= ((int64_t)1 << 32) || kp.M * kp.nkb * 4 >= ((int64_t)1 << 32))
+    return hipErrorNotSupported;
+  kp.tiles_n = (int)(kp.N / 256);
+  kp.tiles_m = (int)((kp.M + 255) / 256);
+  const int64_t nwg = (int64_t)kp.tiles_m * kp.tiles_n;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7FFFFFFF) return hipErrorInvalidValue;
+  kp.nwg = (int)nwg;
+  if (kp.pow2)
+    gemm_contiguous_hybrid_kernel<true, kSwiglu><<<dim3((unsigned)nwg), dim3(512), 0, s>>>(kp);
+  else
+    gemm_contiguous_hybrid_kernel<false, kSwiglu><<<dim3((unsigned)nwg), dim3(512), 0, s>>>(kp);
+  return hipGetLastError();
 }
 
 constexpr size_t kLdsBytes = 163840;  // gfx950 LDS per workgroup
@@ -1782,6 +1912,25 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         pick("tile2_256x128");
         return run_tile2<256, 128, 4, 2, Layout::Dense>(kp, stream);
       }
+      if (!force && p.M > 64 && p.M < 512) {
+        // skinny M: the largest direct-load tile that still gives about 3/4 of the CUs a
+        // workgroup, else the one with the most workgroups (64 x 128). Measured on the decode
+        // layers' shapes at M = 128 and 256: 1.5-1.7x faster than 128 x 128 register-staged
+        // tiles where N / 128 is small (56 workgroups), equal where N is wide
+        const int64_t tn128 = p.N / 128, tn256 = p.N % 256 == 0 ? p.N / 256 : 0;
+        hipError_t e = hipErrorNotSupported;
+        if (((p.M + 255) / 256) * tn128 >= 192) {
+          pick("tile3_256x128");
+          e = run_tile3<256, 128, 4, 2, 3, Layout::Dense>(kp, stream);
+        } else if (((p.M + 127) / 128) * tn256 >= 192) {
+          pick("tile3_128x256");
+          e = run_tile3<128, 256, 2, 4, 3, Layout::Dense>(kp, stream);
+        } else {
+          pick("tile3_64x128");
+          e = run_tile3<64, 128, 2, 4, 3, Layout::Dense>(kp, stream);
+        }
+        if (e != hipErrorNotSupported) return e;
+      }
       pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Dense>(kp, stream);
     case Layout::Masked:
@@ -1811,6 +1960,16 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
         }
         // weights of K block kb+2 issued at the start of K block kb (split issue): measured 5%
         // faster than whole-stage refills on the HBM-bound masked shapes
+        if (is("t3_256x256b")) {
+          pick("tile3_256x256_split");
+          const hipError_t e = run_tile3<256, 256, 2, 4, 2, Layout::Masked, false, true>(kp, stream);
+          if (e != hipErrorNotSupported) return e;
+        }
+        {
+          pick("masked_hybrid_128_256");
+          const hipError_t e = run_masked_hybrid<false>(kp, stream);
+          if (e != hipErrorNotSupported) return e;
+        }
         pick("tile3_256x256_split");
         const hipError_t e = run_tile3<256, 256, 2, 4, 2, Layout::Masked, false, true>(kp, stream);
         if (e != hipErrorNotSupported) return e;
@@ -1820,6 +1979,13 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule sched, int64_t expected_m,
       pick("tile2_128x128");
       return run_tile2<128, 128, 2, 4, Layout::Masked>(kp, stream);
     case Layout::Contiguous:
+      // 256-row tiles over blocks of one expert, 128-row ones elsewhere, where the rounds of
+      // workgroups allow it
+      if ((!force && kp.N % 256 == 0 && contiguous_hybrid_pays(kp)) || is("hybrid")) {
+        pick("contiguous_hybrid_128_256");
+        const hipError_t e = run_contiguous_hybrid<false>(kp, stream);
+        if (e != hipErrorNotSupported) return e;
+      }
       // the three-stage direct-load ring pays off once K is long enough to fill it (measured:
       // 8% faster than the register-staged kernel at K = 2048)
       if (is("t3_128x256b")) {
@@ -1858,6 +2024,10 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
         pick("tile3_swiglu_128x256_split");
         return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true, true>(kp, stream);
       }
+      if (is("hybrid") || (!force && contiguous_hybrid_pays(kp))) {
+        pick("contiguous_hybrid_swiglu_128_256");
+        return run_contiguous_hybrid<true>(kp, stream);
+      }
       pick("tile3_swiglu_128x256");
       return run_tile3<128, 256, 2, 4, 3, Layout::Contiguous, true>(kp, stream);
     case Layout::Masked:
@@ -1869,8 +2039,12 @@ hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int6
         pick("tile3_swiglu_128x256");
         return run_tile3<128, 256, 2, 4, 3, Layout::Masked, true>(kp, stream);
       }
-      pick("tile3_swiglu_256x256_split");
-      return run_tile3<256, 256, 2, 4, 2, Layout::Masked, true, true>(kp, stream);
+      if (is("t3_256x256b")) {
+        pick("tile3_swiglu_256x256_split");
+        return run_tile3<256, 256, 2, 4, 2, Layout::Masked, true, true>(kp, stream);
+      }
+      pick("masked_hybrid_swiglu_128_256");
+      return run_masked_hybrid<true>(kp, stream);
     case Layout::Dense:
       (void)is;
       pick("tile3_swiglu_128x256");

@@ -187,6 +187,26 @@ def test_swiglu_split_issue_is_bitwise_the_same(dg, switches, layout):
         assert torch.equal(hq1[rows], hq2[rows]) and torch.equal(sh1[:, rows], sh2[:, rows])
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_swiglu_contiguous_hybrid_is_bitwise_the_same(dg, switches, pow2):
+    # the contiguous hybrid kernel (256-row tiles over two blocks of one expert, 128-row tiles
+    # elsewhere; forced, since small problems keep the 128-row kernel) gives the 128-row
+    # kernel's hq bytes and scales exactly
+    dev, _, _ = _contiguous_case(dg, 3, 1000, 640, 256, 73, pow2)
+    xq_d, sx_d, w1_d, s1_d, _, _, mi_d = dev
+    firsts = mi_d.cpu().numpy().reshape(-1, 128)[:, 0]
+    pairs = [(firsts[i], firsts[i + 1] if i + 1 < firsts.size else -1) for i in range(0, firsts.size, 2)]
+    assert any(a == b for a, b in pairs) and any(a != b for a, b in pairs)
+    say("swiglu contiguous hybrid ue8m0=%s" % pow2)
+    switches.setenv("DG_TILE", "t3_128x256")
+    hq1, sh1 = dg.gemm_fp8_swiglu(CONTIG, xq_d, sx_d, w1_d, s1_d, mi_d, ue8m0=pow2)
+    switches.setenv("DG_TILE", "hybrid")
+    hq2, sh2 = dg.gemm_fp8_swiglu(CONTIG, xq_d, sx_d, w1_d, s1_d, mi_d, ue8m0=pow2)
+    torch.cuda.synchronize()
+    rows = torch.nonzero(mi_d >= 0).flatten()
+    assert torch.equal(hq1[rows], hq2[rows]) and torch.equal(sh1[:, rows], sh2[:, rows])
+
+
 @pytest.mark.parametrize("case", range(24))
 def test_ffn_random_shapes(dg, case):
     # the whole expert FFN on seeded random shapes, both grouped layouts, both scale types,

@@ -61,12 +61,16 @@ def test_contiguous_parity(dg, G, tokens, N, K):
     assert_close(bf16_values(d), R, "contiguous", mask=omi[:, None].repeat(N, 1) >= 0)
 
 
-@pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None, "t3_128x256b"])
+@pytest.mark.parametrize("variant", ["t3_128x256", "t2_128x128", None, "t3_128x256b", "hybrid"])
 def test_contiguous_tile_kernels(dg, switches, variant):
-    # long enough K for the automatic choice to take the direct-load ring; each kernel checked
-    # against the oracle and against the others bit for bit
+    # experts of 2-4 blocks of 128 rows, so the automatic (hybrid) kernel runs 256-row tiles over
+    # blocks of one expert and 128-row ones where a pair straddles two experts or the end; long
+    # K; each kernel checked against the oracle and against the others bit for bit
     G, N, K = 3, 512, 4352
-    (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 300, N, K, seed=21)
+    (qa, sa, qb, sb, mi), (oqa, osa, oqb, osb, omi) = _both_sides_contiguous(dg, G, 1000, N, K, seed=21)
+    firsts = omi.reshape(-1, 128)[:, 0]
+    pairs = [(firsts[i], firsts[i + 1] if i + 1 < firsts.size else -1) for i in range(0, firsts.size, 2)]
+    assert any(a == b for a, b in pairs) and any(a != b for a, b in pairs)
     if variant:
         switches.setenv("DG_TILE", variant)
     else:
