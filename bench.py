@@ -12,10 +12,11 @@ Steps are captured in HIP graphs (one graph per weight copy, launched on torch's
 and replayed, so the measurement is GPU time rather than Python launch overhead.
 
 Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included).
-`roofline` is for the kernel that takes the most time in the step; its duration comes from
-HIP events, on the stream it runs on, around replays of a graph of back-to-back launches of
-that kernel alone (one per weight copy): at least 100 launches and 10 replays per kernel,
-and the median over the replays. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
+`roofline` is for the kernel that takes the most time in the step. Every kernel is timed
+where it runs in the step: HIP events, on the stream it runs on, between replays (queued back
+to back) of a graph that runs, for each weight copy in turn, the launches that precede the
+kernel in the step and the kernel itself; minus the same for the preceding launches alone.
+At least 100 launches and 10 replays per kernel; medians over the replays. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
 of the same workload. `traffic` (HBM bytes per launch) is read from profiles/traffic.json
 when that file was produced from the current kernel source.
 
@@ -324,6 +325,27 @@ def time_graphs(torch, graphs, n):
     return e0.elapsed_time(e1)
 
 
+def replay_intervals(torch, graph, n):
+    """Per-replay GPU times (ms) of n replays queued back to back, with an event between every
+    two: the host queues them all before the first ends, so no interval holds host launch
+    latency, except possibly the first, which is dropped. (Events around one replay at a time
+    would include that latency: about 36 us per replay, measured on a one-launch graph.)"""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 2)]
+    torch.cuda.synchronize()
+    for i in range(n + 1):
+        ev[i].record()
+        graph.replay()
+    ev[n + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(1, n + 1)]
+
+
+def median(v):
+    v = sorted(v)
+    h = len(v) // 2
+    return v[h] if len(v) % 2 else 0.5 * (v[h - 1] + v[h])
+
+
 def warm_clocks(torch, graphs, seconds):
     """Untimed replays for about `seconds` of wall time: the GPU raises its clocks only after a
     stretch of sustained work, and a short first measurement would catch the ramp."""
@@ -422,42 +444,53 @@ def main():
         def cast_only(L=L):
             dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
 
-        # (label, launch(c), flops and bytes of one launch, part of the step)
-        timed = [("cast", lambda c, L=L: cast_only(L), (0.0, cast_bytes(L["rows"], K)), True)]
+        # (label, launch(c), flops and bytes of one launch, part of the step, the launches that
+        # precede it in the step). A kernel is timed where it runs in the step: graphs of its
+        # preceding launches and itself, minus graphs of the preceding launches alone (so a GEMM
+        # reads activations its cast has just written, as in the step)
+        cast_fn = lambda c, L=L: cast_only(L)
+        timed = [("cast", cast_fn, (0.0, cast_bytes(L["rows"], K)), True, [])]
         if ffn:
             H, I = s_["H"], s_["I"]
+            swiglu_fn = lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
+                                                          L["meta"], expected_m=expected_m(L), hq=L["hq"], sfh=L["sh"],
+                                                          ue8m0=L["ue8m0"])
             timed += [
-                ("swiglu gate/up N=%d K=%d" % (2 * I, H),
-                 lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
-                                                   L["meta"], expected_m=expected_m(L), hq=L["hq"], sfh=L["sh"],
-                                                   ue8m0=L["ue8m0"]),
-                 swiglu_work(s_, L["valid"], L["active"]), True),
+                ("swiglu gate/up N=%d K=%d" % (2 * I, H), swiglu_fn, swiglu_work(s_, L["valid"], L["active"]), True,
+                 [cast_fn]),
                 ("down N=%d K=%d" % (H, I),
                  lambda c, L=L, base=base: grouped(L, base, L["hq"], L["sh"], *L["ws"][c % len(L["ws"])][2:], L["y"]),
-                 layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"], L["active"]), True),
+                 layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"], L["active"]), True, [cast_fn, swiglu_fn]),
                 # the same gate/up product as a plain GEMM with bf16 output: the cost of the epilogue
                 ("plain gate/up (bf16 out, not in the step) N=%d K=%d" % (2 * I, H),
                  lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2], L["d"]),
-                 layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"], L["active"]), False),
+                 layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"], L["active"]), False, [cast_fn]),
             ]
         else:
             timed.append(("gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
                                                                    *L["ws"][c % len(L["ws"])][:2], L["d"]),
-                          layer_work(kind, s_, L["valid"], L["active"]), True))
+                          layer_work(kind, s_, L["valid"], L["active"]), True, [cast_fn]))
         lc = len(L["ws"])
-        for lab, fn, (f, b), in_step in timed:
-            gr = capture(torch, lambda fn=fn, lc=lc: [fn(c) for c in range(lc)])
-            n = max(10, math.ceil(reps / lc))
+        n = max(10, math.ceil(reps / lc))
+
+        def graph_us(seq, lc=lc, n=n):
+            """Per-copy durations (us) of a graph that runs `seq` for each weight copy in turn."""
+            gr = capture(torch, lambda: [f(c) for c in range(lc) for f in seq])
             time_graphs(torch, [gr], 2)
-            per = sorted(time_graphs(torch, [gr], 1) / lc * 1e3 for _ in range(n))
-            avg_us = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+            out = [ms / lc * 1e3 for ms in replay_intervals(torch, gr, n)]
+            del gr
+            return out
+
+        for lab, fn, (f, b), in_step, before in timed:
+            with_it = graph_us(before + [fn])
+            base_us = median(graph_us(before)) if before else 0.0
+            avg_us = median(with_it) - base_us
             bound = "hbm" if (f == 0.0 or f / b < RIDGE) else "mfma"
             layer = kind if ffn else "%s N=%d K=%d" % (kind, s_["N"], K)
             kernels.append({"kernel": lab, "layer": layer, "avg_us": avg_us,
                             "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
                             "bound": bound, "flops": f, "bytes": b, "launches": n * lc, "replays": n,
-                            "mean_us": sum(per) / len(per), "in_step": in_step})
-            del gr
+                            "in_step": in_step})
     dom = max((k for k in kernels if k["in_step"]), key=lambda k: k["avg_us"])
 
     # the whole step: W untimed warmup steps, then exactly K timed steps
