@@ -4,7 +4,8 @@ Default workload ("decode", dense + grouped at decode): two dense DeepSeek-V3-sh
 at M = 64 tokens, (N=7168, K=2048) and (N=24576, K=1536), and the two MoE expert layers in
 the masked layout one GPU holds at decode (G=32 experts, 256-row buffers, valid rows
 ~U{0..256}), (N=4096, K=7168) and (N=7168, K=2048). One step = for each layer, the per-token
-FP8 cast of its fp32 activations followed by its block-scaled FP8 GEMM (bf16 out).
+FP8 cast of its fp32 activations followed by its block-scaled FP8 GEMM (bf16 out). A masked
+layer casts the valid rows of each expert only: the rows its GEMM reads.
 Inputs are resident in HBM before timing starts. Every layer cycles through R_l copies of
 its weights (R_l * |weights_l| >= 512 MiB) so the 256 MiB Infinity Cache cannot serve them.
 
@@ -201,11 +202,20 @@ def expected_m(L):
     return max(1, L["valid"] // L["G"])
 
 
+def cast_layer(dg, L):
+    """The layer's per-token activation cast: in the masked layout, of the valid rows only
+    (the rows its GEMM reads)."""
+    if L["kind"].endswith("masked"):
+        dg.cast_fp8_per_token_masked(L["a"], L["meta"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
+    else:
+        dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
+
+
 def run_layer(dg, L, copy_idx):
     """Cast the layer's activations, then its GEMM with weight copy `copy_idx`."""
     kind = L["kind"]
     u = L["ue8m0"]
-    dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=u)
+    cast_layer(dg, L)
     if kind in FFN_KINDS:
         w1, s1, w2, s2 = L["ws"][copy_idx % len(L["ws"])]
         dg.moe_ffn_fp8(L["layout"], L["qa"], L["sa"], w1, s1, w2, s2, L["meta"], expected_m=expected_m(L),
@@ -442,14 +452,15 @@ def main():
         K = s_["H"] if ffn else s_["K"]
 
         def cast_only(L=L):
-            dg.cast_fp8_per_token(L["a"], L["qa"], L["sa"], ue8m0=L["ue8m0"])
+            cast_layer(dg, L)
 
         # (label, launch(c), flops and bytes of one launch, part of the step, the launches that
         # precede it in the step). A kernel is timed where it runs in the step: graphs of its
         # preceding launches and itself, minus graphs of the preceding launches alone (so a GEMM
         # reads activations its cast has just written, as in the step)
         cast_fn = lambda c, L=L: cast_only(L)
-        timed = [("cast", cast_fn, (0.0, cast_bytes(L["rows"], K)), True, [])]
+        cast_rows = L["valid"] if base == "masked" else L["rows"]
+        timed = [("cast", cast_fn, (0.0, cast_bytes(cast_rows, K)), True, [])]
         if ffn:
             H, I = s_["H"], s_["I"]
             swiglu_fn = lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
@@ -515,7 +526,9 @@ def main():
                             "SwiGLU and FP8 re-cast, then the down GEMM (bf16 out); replayed from HIP graphs"
                             if args.workload in FFN_WORKLOADS else
                             "per-token FP8 cast of fp32 activations + FP8 block-scaled GEMM (bf16 out), "
-                            "per layer; replayed from HIP graphs")},
+                            "per layer; replayed from HIP graphs")
+                           + ("; masked layers cast their valid rows only" if any(
+                               k.endswith("masked") for k, _ in wl["layers"]) else "")},
         "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5),
         "roofline": {"bound": dom["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -89,6 +89,20 @@ dg_status_t dg_cast_fp8_per_token(const void* x, dg_input_dtype_t x_dtype, int64
                                   int64_t K, uint8_t* q, float* sf, void* stream);
 
 /*
+ * The per-token cast of the masked layout's activations, valid rows only: x, q, sf as above
+ * with G groups of M_max rows; of group g only rows m < masked_m[g] (clamped to [0, M_max])
+ * are cast, the others' codes and scales are not written. Those are exactly the rows the
+ * masked grouped GEMM reads (it never reads an activation row at or beyond masked_m[g]), so
+ * in a masked layer this cast does the same job with the padding rows skipped.
+ *   scale_fmt: DG_SCALE_F32 (the rule above) or DG_SCALE_UE8M0 (dg_cast_fp8_per_token_ue8m0).
+ *   masked_m: [G] int32, device, 16-byte aligned (read on the device).
+ * Same requirements and errors as dg_cast_fp8_per_token.
+ */
+dg_status_t dg_cast_fp8_per_token_masked(const void* x, dg_input_dtype_t x_dtype, int32_t scale_fmt, int32_t G,
+                                         int64_t M_max, int64_t K, const int32_t* masked_m, uint8_t* q, float* sf,
+                                         void* stream);
+
+/*
  * Per-block FP8 cast of weights: the same rule as above with the amax taken over each
  * 128x128 block (DeepSeek-V3 repo review, "Solution philosophy": 128x128 block scaling).
  *   w  [N,K] fp32 or bf16; q [N,K] e4m3 (output); sf [N/128, K/128] fp32 (output).

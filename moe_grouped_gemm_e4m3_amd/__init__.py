@@ -14,6 +14,7 @@ include/dg.h specifies; weight scales are [N/128, K/128].
 Entry points (same names as the C ABI, without the dg_ prefix):
   cast_fp8_per_token(x)                      -> (q [M,K] uint8, sf [K/128,M] fp32)
                                                 (x [G,M,K] -> q [G,M,K], sf [G,K/128,M])
+  cast_fp8_per_token_masked(x, masked_m)     -> (q [G,M_max,K], sf [G,K/128,M_max]): valid rows only
   cast_fp8_per_block(w)                      -> (q [N,K] uint8, sf [N/128,K/128] fp32)
   convert_fp8_e4m3(x)                        -> q uint8: the hardware conversion of the SwiGLU epilogue
   gemm_fp8_nt(a, sfa, b, sfb)                -> d [M,N] bf16
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
             for fn in ("dg_cast_fp8_per_token", "dg_cast_fp8_per_block", "dg_gemm_fp8_nt",
                        "dg_grouped_gemm_contiguous", "dg_grouped_gemm_masked"):
                 getattr(L, fn + sfx).restype = ctypes.c_int
+        L.dg_cast_fp8_per_token_masked.argtypes = [P, ctypes.c_int, I32, I32, I64, I64, P, P, P, P]
+        L.dg_cast_fp8_per_token_masked.restype = ctypes.c_int
         L.dg_gemm_fp8_scheduled.argtypes = [I32, I32, I32, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_gemm_fp8_swiglu.argtypes = [I32, I32, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
         L.dg_moe_ffn_fp8.argtypes = [I32, I32, P, P, P, P, P, P, P, P, P, P, I32, I64, I64, I64, I64, P]
@@ -134,6 +137,29 @@ def cast_fp8_per_token(x: torch.Tensor, q: torch.Tensor | None = None, sf: torch
     dt = INPUT_BF16 if x.dtype == torch.bfloat16 else INPUT_F32
     fn = lib().dg_cast_fp8_per_token_ue8m0 if ue8m0 else lib().dg_cast_fp8_per_token
     _check(fn(_ptr(x), dt, G, M, K, _ptr(q), _ptr(sf), _stream(x.device)))
+    return q, sf
+
+
+def cast_fp8_per_token_masked(x: torch.Tensor, masked_m: torch.Tensor, q: torch.Tensor | None = None,
+                              sf: torch.Tensor | None = None, ue8m0: bool = False):
+    """x [G,M_max,K] fp32/bf16, masked_m [G] int32 -> (q [G,M_max,K] uint8, sf [G,K/128,M_max]):
+    the per-token cast of rows m < masked_m[g] only; other rows of q and sf are not written."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, x.dtype, "x")
+    _need(masked_m, torch.int32, "masked_m")
+    if x.dim() != 3:
+        raise ValueError("x must be [G,M_max,K]")
+    G, M, K = x.shape
+    if tuple(masked_m.shape) != (G,):
+        raise ValueError("masked_m must be [G]")
+    q = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if q is None else q
+    sf = torch.empty((G, K // 128, M), dtype=torch.float32, device=x.device) if sf is None else sf
+    if tuple(q.shape) != tuple(x.shape) or tuple(sf.shape) != (G, K // 128, M):
+        raise ValueError("q %s / sf %s do not match x %s" % (tuple(q.shape), tuple(sf.shape), tuple(x.shape)))
+    dt = INPUT_BF16 if x.dtype == torch.bfloat16 else INPUT_F32
+    _check(lib().dg_cast_fp8_per_token_masked(_ptr(x), dt, SCALE_UE8M0 if ue8m0 else SCALE_F32, G, M, K,
+                                              _ptr(masked_m), _ptr(q), _ptr(sf), _stream(x.device)))
     return q, sf
 
 

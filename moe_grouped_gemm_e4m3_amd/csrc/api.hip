@@ -98,9 +98,11 @@ dg_status_t run_gemm(dg::Layout layout, int schedule, bool pow2, const uint8_t* 
 }
 
 dg_status_t run_cast(bool per_block, bool pow2, const void* x, dg_input_dtype_t dtype, int64_t groups, int64_t rows,
-                     int64_t K, uint8_t* q, float* sf, void* stream) {
-  const char* name = per_block ? (pow2 ? "dg_cast_fp8_per_block_ue8m0" : "dg_cast_fp8_per_block")
-                               : (pow2 ? "dg_cast_fp8_per_token_ue8m0" : "dg_cast_fp8_per_token");
+                     int64_t K, uint8_t* q, float* sf, void* stream, const int32_t* masked_m = nullptr,
+                     const char* name = nullptr) {
+  if (!name)
+    name = per_block ? (pow2 ? "dg_cast_fp8_per_block_ue8m0" : "dg_cast_fp8_per_block")
+                     : (pow2 ? "dg_cast_fp8_per_token_ue8m0" : "dg_cast_fp8_per_token");
   if (dtype != DG_INPUT_F32 && dtype != DG_INPUT_BF16) return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", name, (int)dtype);
   if (groups < 0 || rows < 0 || K < 0) return fail(DG_ERR_INVALID_ARGUMENT, "%s: negative size", name);
   if (K % kQ != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "%s: K=%lld is not a multiple of 128", name, (long long)K);
@@ -110,11 +112,12 @@ dg_status_t run_cast(bool per_block, bool pow2, const void* x, dg_input_dtype_t 
   if (groups == 0 || rows == 0 || K == 0) return ok();
   if (!x || !q || !sf) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
+  if (masked_m && !aligned16(masked_m)) return fail(DG_ERR_MISALIGNED, "%s: every pointer must be 16-byte aligned", name);
   dg_status_t st = check_device();
   if (st != DG_OK) return st;
   hipError_t e = per_block ? dg::launch_cast_per_block(x, dtype == DG_INPUT_BF16, pow2, rows, K, q, sf,
                                                        static_cast<hipStream_t>(stream))
-                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, pow2, groups, rows, K, q, sf,
+                           : dg::launch_cast_per_token(x, dtype == DG_INPUT_BF16, pow2, groups, rows, K, masked_m, q, sf,
                                                        static_cast<hipStream_t>(stream));
   return launched(e, name);
 }
@@ -223,6 +226,16 @@ dg_status_t dg_cast_fp8_per_token_ue8m0(const void* x, dg_input_dtype_t x_dtype,
 dg_status_t dg_cast_fp8_per_block_ue8m0(const void* w, dg_input_dtype_t w_dtype, int64_t N, int64_t K, uint8_t* q,
                                         float* sf, void* stream) {
   return run_cast(true, true, w, w_dtype, 1, N, K, q, sf, stream);
+}
+
+dg_status_t dg_cast_fp8_per_token_masked(const void* x, dg_input_dtype_t x_dtype, int32_t scale_fmt, int32_t G,
+                                         int64_t M_max, int64_t K, const int32_t* masked_m, uint8_t* q, float* sf,
+                                         void* stream) {
+  const char* name = "dg_cast_fp8_per_token_masked";
+  if (scale_fmt != DG_SCALE_F32 && scale_fmt != DG_SCALE_UE8M0)
+    return fail(DG_ERR_INVALID_ARGUMENT, "%s: unknown scale format %d", name, scale_fmt);
+  if (G > 0 && M_max > 0 && K > 0 && !masked_m) return fail(DG_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+  return run_cast(false, scale_fmt == DG_SCALE_UE8M0, x, x_dtype, G, M_max, K, q, sf, stream, masked_m, name);
 }
 
 dg_status_t dg_gemm_fp8_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,

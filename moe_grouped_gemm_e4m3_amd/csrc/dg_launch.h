@@ -42,8 +42,10 @@ hipError_t launch_gemm(const GemmProblem& p, Schedule s, int64_t expected_m, hip
 hipError_t launch_gemm_swiglu(const GemmProblem& p, uint8_t* hq, float* sh, int64_t expected_m, hipStream_t stream,
                               const char** chosen);
 
-hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, int64_t M, int64_t K, uint8_t* q,
-                                 float* sf, hipStream_t stream);
+// Per-token cast of G groups of M rows; masked_m (or nullptr): only rows r < masked_m[g] of
+// group g are cast, the others left unwritten.
+hipError_t launch_cast_per_token(const void* x, int bf16, int pow2, int64_t G, int64_t M, int64_t K,
+                                 const int32_t* masked_m, uint8_t* q, float* sf, hipStream_t stream);
 // x [n] fp32 -> q [n] e4m3 with the hardware conversion (n % 4 == 0, n > 0).
 hipError_t launch_convert_e4m3(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
 hipError_t launch_cast_per_block(const void* w, int bf16, int pow2, int64_t N, int64_t K, uint8_t* q, float* sf,

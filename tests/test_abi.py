@@ -71,6 +71,17 @@ def test_convert_argument_errors(L):
     assert L.dg_convert_fp8_e4m3(None, 0, None, None) == 0  # empty: nothing enqueued
 
 
+def test_masked_cast_argument_errors(L):
+    c = L.dg_cast_fp8_per_token_masked
+    assert c(P, 0, 0, 4, 64, 500, P, P, P, None) == 2    # K not a multiple of 128
+    assert c(P, 2, 0, 4, 64, 512, P, P, P, None) == 1    # unknown dtype
+    assert c(P, 0, 7, 4, 64, 512, P, P, P, None) == 1    # unknown scale format
+    assert c(P, 0, 0, -1, 64, 512, P, P, P, None) == 1
+    assert c(P, 0, 0, 4, 64, 512, None, P, P, None) == 1  # masked_m null
+    assert c(P, 0, 0, 4, 64, 512, Q, P, P, None) == 3
+    assert c(None, 0, 0, 0, 64, 512, None, None, None, None) == 0  # G = 0: nothing enqueued
+
+
 def test_status_strings(L):
     for code, name in [(0, b"DG_OK"), (1, b"DG_ERR_INVALID_ARGUMENT"), (2, b"DG_ERR_UNSUPPORTED_SHAPE"),
                        (3, b"DG_ERR_MISALIGNED"), (4, b"DG_ERR_UNSUPPORTED_DEVICE"), (5, b"DG_ERR_LAUNCH")]:
@@ -105,6 +116,7 @@ def test_gemm_without_gpu_reports_device(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _gemm(L) == 4  # arguments valid, no gfx950 device: nothing launched
+    assert L.dg_cast_fp8_per_token_masked(P, 0, 1, 4, 64, 512, P, P, P, None) == 4
 
 
 def test_grouped_argument_errors(L):

@@ -247,3 +247,55 @@ def test_cast_prefill_activation_full_size(dg):
     qo, so = oracle.cast_per_token(a)
     assert_same_bytes(q, qo, "prefill q")
     assert_same_bits(s, kmajor(so), "prefill s")
+
+
+def _masked_cast_check(dg, x, mm, ue8m0, what):
+    """The masked cast on the GPU against the oracle's cast of the valid rows, bit for bit;
+    rows at or beyond masked_m keep their sentinel bytes in q and sf."""
+    G, M, K = x.shape
+    xt = x if isinstance(x, torch.Tensor) else torch.from_numpy(x)
+    q = torch.full((G, M, K), 0xAB, dtype=torch.uint8, device="cuda:0")
+    sf = torch.full((G, K // 128, M), -1, dtype=torch.int32, device="cuda:0").view(torch.float32)
+    dg.cast_fp8_per_token_masked(xt.to("cuda:0"), to_dev(np.asarray(mm, np.int32)), q=q, sf=sf, ue8m0=ue8m0)
+    qh, sh = q.cpu().numpy(), sf.view(torch.int32).cpu().numpy()
+    xf = xt.float().numpy()
+    for g in range(G):
+        v = int(min(max(mm[g], 0), M))
+        if v:
+            qo, so = oracle.cast_per_token(xf[g, :v], pow2=ue8m0)
+            assert np.array_equal(qh[g, :v], qo), "%s: codes of group %d" % (what, g)
+            assert np.array_equal(sh[g, :, :v], kmajor(so).view(np.int32)), "%s: scales of group %d" % (what, g)
+        assert (qh[g, v:] == 0xAB).all(), "%s: codes written beyond masked_m in group %d" % (what, g)
+        assert (sh[g, :, v:] == -1).all(), "%s: scales written beyond masked_m in group %d" % (what, g)
+
+
+@pytest.mark.parametrize("ue8m0", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_cast_per_token_masked(dg, dtype, ue8m0):
+    # empty, one-row, partial, full, over-full and negative counts; 5 K blocks (a ragged pair)
+    G, M, K = 6, 200, 640
+    mm = [0, 1, 63, 200, 250, -3]
+    x = synth.with_outliers(synth.normal((G, M, K), 12, synth.TID_A), 12)
+    say("cast masked %s ue8m0=%s" % (dtype, ue8m0))
+    _masked_cast_check(dg, torch.from_numpy(x).to(dtype), mm, ue8m0, "masked cast")
+
+
+@pytest.mark.slow
+def test_cast_per_token_masked_full_size(dg):
+    # the masked decode layers' activations: 32 experts x 256-row buffers x 7168, valid ~U{0..256}
+    G, M, K = 32, 256, 7168
+    mm = synth.masked_layout(G, M, 0)
+    x = synth.normal((G, M, K), 13, synth.TID_A)
+    say("cast masked full size 32x256x7168")
+    _masked_cast_check(dg, x, mm, False, "masked cast full size")
+
+
+def test_cast_per_token_masked_many_groups(dg):
+    # more groups than a wave has lanes (the valid rows are numbered 64 groups at a time):
+    # empty groups at and around the chunk boundaries, full and over-full ones
+    G, M, K = 150, 9, 256
+    mm = synth.masked_layout(G, M, 5)
+    mm[[0, 63, 64, 65, 127, 128, 149]] = [0, 0, 9, 0, 20, -1, 9]
+    x = synth.normal((G, M, K), 14, synth.TID_A)
+    say("cast masked 150 groups")
+    _masked_cast_check(dg, x, mm, False, "masked cast 150 groups")
