@@ -288,3 +288,23 @@ def test_masked_full_size_sampled(dg, N, K):
     assert_close(y[rows, cc], R, "masked full %dx%d" % (N, K))
     for g in range(G):
         assert (bits[g, int(omm[g]):] == SENTINEL).all()
+
+
+@pytest.mark.parametrize("G", [64, 65])
+def test_masked_hybrid_group_order(dg, G):
+    # the automatic masked kernel takes up to 64 groups in descending order of their valid rows
+    # (ties by index), more in index order: many ties, empty, full and over-full groups
+    M_max, N, K = 200, 256, 256
+    mm = synth.masked_layout(G, M_max, 40 + G)
+    mm[::7] = 0
+    mm[1::9] = M_max
+    mm[2::11] = 77
+    mm[3] = 500
+    (qa, sa, qb, sb, mmd), (oqa, osa, oqb, osb, omm) = _both_sides_masked(dg, G, M_max, N, K, 41, mm)
+    d = torch.full((G, M_max, N), SENTINEL, dtype=torch.int16, device="cuda:0").view(torch.bfloat16)
+    say("masked hybrid group order G=%d" % G)
+    dg.grouped_gemm_masked(qa, sa, qb, sb, mmd, d=d)
+    R = oracle.grouped_masked(oqa, osa, oqb, osb, omm)
+    valid = np.isfinite(R)
+    assert_close(bf16_values(d), R, "masked group order G=%d" % G, mask=valid)
+    assert (d.view(torch.int16).cpu().numpy()[~valid] == SENTINEL).all()
