@@ -13,11 +13,15 @@ Steps are captured in HIP graphs (one graph per weight copy, launched on torch's
 and replayed, so the measurement is GPU time rather than Python launch overhead.
 
 Prints ONE JSON line. `value` is the GEMM FLOP rate over the whole step (cast included).
-`roofline` is for the kernel that takes the most time in the step. Every kernel is timed
-where it runs in the step: HIP events, on the stream it runs on, between replays (queued back
-to back) of a graph that runs, for each weight copy in turn, the launches that precede the
-kernel in the step and the kernel itself; minus the same for the preceding launches alone.
-At least 100 launches and 10 replays per kernel; medians over the replays. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
+`roofline` is for the kernel that takes the most time in the step. Times come from HIP
+events on the stream the kernels run on, between replays of graphs queued back to back, and
+are medians over at least 10 replays and 100 launches. Each kernel gets two:
+`in_step_us`, its marginal time in the step (a graph of the whole step over every weight
+copy, minus the same graph without that one launch, the two alternating in three blocks of
+replays), and `avg_us`, its launch duration (a graph of back-to-back launches of it alone
+through the weight copies, >= 8 launches and about 200 us of work per graph). The roofline
+uses `avg_us`, the figure a kernel trace reports. A cast timed alone reads an input that its
+previous launch left in the caches, unlike in the step. `cpu_baseline` is the CPU oracle on the host cores over a bounded sample
 of the same workload. `traffic` (HBM bytes per launch) is read from profiles/traffic.json
 when that file was produced from the current kernel source.
 
@@ -444,65 +448,91 @@ def main():
         else:
             dg.grouped_gemm_masked(a, sa, qb, sb, L["meta"], expected_m=expected_m(L), d=d, ue8m0=u)
 
-    for L in layers:
+    def seq_graph(launches, nc):
+        """A graph that runs `launches` (each launch(c)) for weight copy c = 0 .. nc-1 in turn."""
+        return capture(torch, lambda: [f(c) for c in range(nc) for f in launches])
+
+    def paired_us(ga, gb, nc, n, blocks=3):
+        """Median per-copy durations (us) of graphs ga and gb, replayed in alternating blocks of
+        n back-to-back replays (so a drift of the clocks affects both alike)."""
+        time_graphs(torch, [ga, gb], 2)
+        ta, tb = [], []
+        for _ in range(blocks):
+            ta += [ms / nc * 1e3 for ms in replay_intervals(torch, ga, n)]
+            tb += [ms / nc * 1e3 for ms in replay_intervals(torch, gb, n)]
+        return median(ta), median(tb)
+
+    # (layer index, label, launch(c), flops and bytes of one launch, part of the step, the
+    # launches that precede it in its layer)
+    entries = []
+    for li, L in enumerate(layers):
         s_ = L["s"]
         kind = L["kind"]
         ffn = kind in FFN_KINDS
         base = kind[4:] if ffn else kind
         K = s_["H"] if ffn else s_["K"]
-
-        def cast_only(L=L):
-            cast_layer(dg, L)
-
-        # (label, launch(c), flops and bytes of one launch, part of the step, the launches that
-        # precede it in the step). A kernel is timed where it runs in the step: graphs of its
-        # preceding launches and itself, minus graphs of the preceding launches alone (so a GEMM
-        # reads activations its cast has just written, as in the step)
-        cast_fn = lambda c, L=L: cast_only(L)
+        cast_fn = lambda c, L=L: cast_layer(dg, L)
         cast_rows = L["valid"] if base == "masked" else L["rows"]
-        timed = [("cast", cast_fn, (0.0, cast_bytes(cast_rows, K)), True, [])]
+        entries.append((li, "cast", cast_fn, (0.0, cast_bytes(cast_rows, K)), True, []))
         if ffn:
             H, I = s_["H"], s_["I"]
             swiglu_fn = lambda c, L=L: dg.gemm_fp8_swiglu(L["layout"], L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2],
                                                           L["meta"], expected_m=expected_m(L), hq=L["hq"], sfh=L["sh"],
                                                           ue8m0=L["ue8m0"])
-            timed += [
-                ("swiglu gate/up N=%d K=%d" % (2 * I, H), swiglu_fn, swiglu_work(s_, L["valid"], L["active"]), True,
-                 [cast_fn]),
-                ("down N=%d K=%d" % (H, I),
+            entries += [
+                (li, "swiglu gate/up N=%d K=%d" % (2 * I, H), swiglu_fn, swiglu_work(s_, L["valid"], L["active"]),
+                 True, [cast_fn]),
+                (li, "down N=%d K=%d" % (H, I),
                  lambda c, L=L, base=base: grouped(L, base, L["hq"], L["sh"], *L["ws"][c % len(L["ws"])][2:], L["y"]),
                  layer_work(base, dict(G=s_["G"], N=H, K=I), L["valid"], L["active"]), True, [cast_fn, swiglu_fn]),
                 # the same gate/up product as a plain GEMM with bf16 output: the cost of the epilogue
-                ("plain gate/up (bf16 out, not in the step) N=%d K=%d" % (2 * I, H),
+                (li, "plain gate/up (bf16 out, not in the step) N=%d K=%d" % (2 * I, H),
                  lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"], *L["ws"][c % len(L["ws"])][:2], L["d"]),
                  layer_work(base, dict(G=s_["G"], N=2 * I, K=H), L["valid"], L["active"]), False, [cast_fn]),
             ]
         else:
-            timed.append(("gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
-                                                                   *L["ws"][c % len(L["ws"])][:2], L["d"]),
-                          layer_work(kind, s_, L["valid"], L["active"]), True, [cast_fn]))
+            entries.append((li, "gemm", lambda c, L=L, base=base: grouped(L, base, L["qa"], L["sa"],
+                                                                          *L["ws"][c % len(L["ws"])][:2], L["d"]),
+                            layer_work(kind, s_, L["valid"], L["active"]), True, [cast_fn]))
+
+    # Two times per kernel:
+    #  - in_step_us: its marginal time in the step, the step graph over every weight copy minus
+    #    the same graph without that one launch (with the step's cache state, inputs and
+    #    neighbours; the cost of a graph replay cancels). Kernels outside the step: none.
+    #  - avg_us: its launch duration, from a graph of back-to-back launches of it alone cycling
+    #    through the weight copies, at least 8 launches and about 200 us of work per graph (so a
+    #    replay's own cost is spread thin). The roofline uses this one, as a kernel trace would.
+    step_seq = [(li, lab, fn) for li, lab, fn, _, in_step, _ in entries if in_step]
+    n_step = max(10, math.ceil(reps / copies))
+    full_graph = seq_graph([fn for _, _, fn in step_seq], copies)
+    for li, lab, fn, (f, b), in_step, before in entries:
+        L = layers[li]
         lc = len(L["ws"])
-        n = max(10, math.ceil(reps / lc))
-
-        def graph_us(seq, lc=lc, n=n):
-            """Per-copy durations (us) of a graph that runs `seq` for each weight copy in turn."""
-            gr = capture(torch, lambda: [f(c) for c in range(lc) for f in seq])
-            time_graphs(torch, [gr], 2)
-            out = [ms / lc * 1e3 for ms in replay_intervals(torch, gr, n)]
-            del gr
-            return out
-
-        for lab, fn, (f, b), in_step, before in timed:
-            with_it = graph_us(before + [fn])
-            base_us = median(graph_us(before)) if before else 0.0
-            avg_us = median(with_it) - base_us
-            bound = "hbm" if (f == 0.0 or f / b < RIDGE) else "mfma"
-            layer = kind if ffn else "%s N=%d K=%d" % (kind, s_["N"], K)
-            kernels.append({"kernel": lab, "layer": layer, "avg_us": avg_us,
-                            "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
-                            "bound": bound, "flops": f, "bytes": b, "launches": n * lc, "replays": n,
-                            "in_step": in_step})
-    dom = max((k for k in kernels if k["in_step"]), key=lambda k: k["avg_us"])
+        marginal = None
+        if in_step:
+            g_without = seq_graph([g for lj, lb, g in step_seq if (lj, lb) != (li, lab)], copies)
+            t_full, t_without = paired_us(full_graph, g_without, copies, n_step)
+            del g_without
+            marginal = t_full - t_without
+            est = max(marginal, 1.0)
+        else:
+            est = 100.0
+        per_graph = lc * max(1, math.ceil(max(8.0, 200.0 / est) / lc))  # launches per graph
+        g_alone = seq_graph([fn], per_graph)
+        n = max(10, math.ceil(reps / per_graph))
+        time_graphs(torch, [g_alone], 2)
+        avg_us = median([ms / per_graph * 1e3 for ms in replay_intervals(torch, g_alone, n)])
+        del g_alone
+        kind = L["kind"]
+        ffn = kind in FFN_KINDS
+        bound = "hbm" if (f == 0.0 or f / b < RIDGE) else "mfma"
+        layer = kind if ffn else "%s N=%d K=%d" % (kind, L["s"]["N"], L["s"]["K"])
+        kernels.append({"kernel": lab, "layer": layer, "avg_us": avg_us, "in_step_us": marginal,
+                        "tflops": f / (avg_us * 1e-6) / 1e12, "gbs": b / (avg_us * 1e-6) / 1e9,
+                        "bound": bound, "flops": f, "bytes": b, "launches": n * per_graph, "replays": n,
+                        "in_step": in_step})
+    del full_graph
+    dom = max((k for k in kernels if k["in_step"]), key=lambda k: k["in_step_us"])
 
     # the whole step: W untimed warmup steps, then exactly K timed steps
     warm_clocks(torch, step_graphs, 0.2)
