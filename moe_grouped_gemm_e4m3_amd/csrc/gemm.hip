@@ -1464,11 +1464,23 @@ __global__ __launch_bounds__(512) void gemm_masked_hybrid_kernel(KParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kBytes];
   __shared__ __attribute__((aligned(16))) float sSB[2][kMaxKb3];
   int g, tm, tn;
-  // no XCD remap: the column tiles of a group go to all XCDs in turn, so every XCD gets a
-  // mix of large and small groups (measured on 32 groups x 256 rows at N=7168, K=2048: 2-13%
-  // faster than four whole groups per XCD, and never slower)
-  tile_of(p, blockIdx.x, true, g, tm, tn);  // tm counts 256-row tiles
-  if (p.sort_groups) g = group_by_rank(p, g);
+  if (p.sort_groups) {
+    // at most two rounds: each XCD takes whole groups (a group's activation rows stay in one
+    // L2), dealt by rank in a snake so that every XCD gets a like mix of large and small
+    // groups, the largest first (slot k of XCD x: rank 8k + x, or 8k + 7 - x for odd k)
+    tile_of(p, xcd_remap(blockIdx.x, (uint32_t)p.nwg), true, g, tm, tn);  // tm counts 256-row tiles
+    int rank = g;
+    if (p.G % 8 == 0) {
+      const int per = p.G / 8, x = g / per, k = g % per;
+      rank = k * 8 + ((k & 1) ? 7 - x : x);
+    }
+    g = group_by_rank(p, rank);
+  } else {
+    // more rounds: groups in order, without the XCD remap, so that a group's column tiles go to
+    // all XCDs in turn (measured on 32 groups x 256 rows at N=7168, K=2048: 2-13% faster than
+    // four whole groups per XCD, and 5-8% faster than any order by size)
+    tile_of(p, blockIdx.x, true, g, tm, tn);
+  }
   const int64_t left = clamp_rows(p.masked_m[g], p.M) - (int64_t)tm * 256;
   if (left <= 128)  // also the tiles with no valid row: the body returns at once
     tile3_main<128, 256, 2, 4, 3, Layout::Masked, kPow2, kSwiglu, false>(p, smem, sSB, g, 2 * tm, tn);
@@ -1622,8 +1634,8 @@ hipError_t run_masked_hybrid(KParams kp, hipStream_t s) {
   kp.nwg = (int)nwg;
   // groups by descending valid rows when the grid is at most two rounds of workgroups: the
   // largest tiles start first and the smallest fill the end (measured on 32 groups x 256 rows,
-  // valid ~U{0..256}: 2.5-4.5% faster at N=4096, K=7168, 512 workgroups); with more rounds
-  // the groups in order (4-7% slower sorted at N=7168, K=2048, 896 workgroups)
+  // valid ~U{0..256}, N=4096, K=7168, 512 workgroups: 4-7% faster than in order with the XCD
+  // remap); with more rounds the groups in order (sorted: 5-8% slower at N=7168, K=2048)
   kp.sort_groups = kp.G <= 64 && nwg <= 2 * (int64_t)cu_count();
   if (kp.pow2)
     gemm_masked_hybrid_kernel<true, kSwiglu><<<dim3((unsigned)nwg), dim3(512), 0, s>>>(kp);

@@ -290,10 +290,11 @@ def test_masked_full_size_sampled(dg, N, K):
         assert (bits[g, int(omm[g]):] == SENTINEL).all()
 
 
-@pytest.mark.parametrize("G", [64, 65])
+@pytest.mark.parametrize("G", [64, 12, 65])
 def test_masked_hybrid_group_order(dg, G):
     # the automatic masked kernel takes up to 64 groups in descending order of their valid rows
-    # (ties by index), more in index order: many ties, empty, full and over-full groups
+    # (ties by index; dealt over the XCDs in a snake when G % 8 == 0), more in index order: many
+    # ties, empty, full and over-full groups
     M_max, N, K = 200, 256, 256
     mm = synth.masked_layout(G, M_max, 40 + G)
     mm[::7] = 0
