@@ -39,7 +39,7 @@ def _cast_both(dg, a, b, pow2):
     return (qa_d, sa_d, qb_d, sb_d), (qa, sa, qb, sb)
 
 
-@pytest.mark.parametrize("case", range(48))
+@pytest.mark.parametrize("case", range(96))
 def test_random_dense(dg, case):
     r = np.random.default_rng(1000 + case)
     M, N, K = int(r.integers(1, 700)), 128 * int(r.integers(1, 9)), 128 * int(r.integers(1, 25))
@@ -51,7 +51,7 @@ def test_random_dense(dg, case):
     assert_close(bf16_values(d), oracle.gemm(oqa, osa, oqb, osb), "random dense case %d" % case)
 
 
-@pytest.mark.parametrize("case", range(20))
+@pytest.mark.parametrize("case", range(48))
 def test_random_contiguous(dg, case):
     r = np.random.default_rng(3000 + case)
     G, tokens = int(r.integers(1, 7)), int(r.integers(1, 900))
@@ -65,7 +65,7 @@ def test_random_contiguous(dg, case):
     assert_close(bf16_values(d), R, "random contiguous case %d" % case, mask=mi[:, None].repeat(N, 1) >= 0)
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_random_masked(dg, case):
     r = np.random.default_rng(5000 + case)
     G, M_max = int(r.integers(1, 7)), int(r.integers(1, 300))
