@@ -388,8 +388,8 @@ def main():
                     help="also run a 256 MiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path (see the sharding "
-              "notes in the design document); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs each GEMM on one device and has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
