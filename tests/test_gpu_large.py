@@ -188,3 +188,51 @@ def test_dense_weights_beyond_32_bit_offsets(dg, switches, capfd):
     rr, cc = np.repeat(np.arange(M), cols.size), np.tile(cols % (128 * P_BLOCKS), M)
     R = oracle.gemm_pairs(oqa, osa, oqbp[0], osbp[0], rr, cc)
     assert_close(y.reshape(-1), R, "dense N=%d K=%d" % (N, K))
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "masked"])
+def test_grouped_weights_beyond_32_bit_offsets(dg, switches, capfd, layout):
+    # one expert whose weights reach 2^32 bytes (N*K per group), 256 rows of which 200 are
+    # routed / valid
+    G, M, N, rows_valid = 1, 256, WRAP_ROWS + 128, 200
+    say("large %s N*K >= 2^32: G=%d M=%d N=%d K=%d" % (layout, G, M, N, K))
+    a = synth.normal((M, K), 15, synth.TID_A)
+    qa, sa = dg.cast_fp8_per_token(torch.from_numpy(a).to(dev()))
+    oqa, osa = oracle.cast_per_token(a)
+    assert_same_bytes(qa, oqa, "A cast")
+    assert_same_bits(sa, kmajor(osa), "A scales")
+    (qbp, sbp), (oqbp, osbp) = _weights(dg, 1, 128 * P_BLOCKS, seed=15)
+    idx = torch.arange(N, device=dev(), dtype=torch.int64) % (128 * P_BLOCKS)
+    qb = qbp[0].index_select(0, idx).view(G, N, K)
+    sb = sbp[0].index_select(0, torch.arange(N // 128, device=dev(), dtype=torch.int64) % P_BLOCKS).view(G, N // 128, K // 128)
+    sentinel = 0x7FBF
+    if layout == "contiguous":
+        mi = np.full(M, -1, np.int32)
+        mi[:rows_valid] = 0
+        d = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+        d.view(torch.int16).fill_(sentinel)
+        meta = torch.from_numpy(mi).to(dev())
+        switches.setenv("DG_LOG", "1")
+        capfd.readouterr()
+        dg.grouped_gemm_contiguous(qa, sa, qb, sb, meta, d=d)
+        assert _chosen(capfd) == ["tile2_128x128"]  # N is an odd multiple of 128
+        out = d
+    else:
+        d = torch.empty((G, M, N), dtype=torch.bfloat16, device=dev())
+        d.view(torch.int16).fill_(sentinel)
+        meta = torch.tensor([rows_valid], dtype=torch.int32, device=dev())
+        switches.setenv("DG_LOG", "1")
+        capfd.readouterr()
+        dg.grouped_gemm_masked(qa.view(G, M, K), sa.view(G, K // 128, M), qb, sb, meta, d=d)
+        assert _chosen(capfd) == ["tile2_256x128"]
+        out = d[0]
+        # rows at or beyond the count keep their bytes
+        assert bool((out[rows_valid:, ::4099].view(torch.int16) == sentinel).all())
+    r = synth.rng(15, 97)
+    cols = np.unique(np.concatenate([np.arange(0, 256), np.arange(WRAP_ROWS - 256, N), r.integers(0, N, 768)]))
+    y = bf16_values(out[:rows_valid].index_select(1, torch.from_numpy(cols).to(dev())))
+    del qb, sb, d, out
+    _free()
+    rr, cc = np.repeat(np.arange(rows_valid), cols.size), np.tile(cols % (128 * P_BLOCKS), rows_valid)
+    R = oracle.gemm_pairs(oqa, osa, oqbp, osbp, rr, cc, group_of_row=np.zeros(M, np.int32))
+    assert_close(y.reshape(-1), R, "%s N=%d K=%d" % (layout, N, K))
